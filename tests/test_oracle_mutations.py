@@ -1,0 +1,104 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each one.
+
+Every mutation below is a slip someone could make while writing the oracle from the pages:
+a swapped nibble order, the wrong tensor-scale divisor, ties rounded away from even, a dropped
+low-rank term, a transposed factor, a sign slip or a dropped block in the GEMV. Each must make
+at least one of the pins in the other oracle test modules fail.
+"""
+import numpy as np
+
+import oracle as O
+import oracle.attnq_oracle as OM
+import test_oracle_gemv as PG
+import test_oracle_quantize as PQ
+import test_oracle_reconstruct as PR
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_swapped_nibbles_are_caught(monkeypatch, golden_dir):
+    orig = OM.quantize_segment
+
+    def swapped(W):
+        c, s, t = orig(W)
+        return ((c >> 4) | (c << 4)).astype(np.uint8), s, t
+    monkeypatch.setattr(OM, "quantize_segment", swapped)
+    assert _fails(PQ.test_hand_worked_example, golden_dir)
+
+
+def test_wrong_tensor_scale_divisor_is_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(OM, "TS_DIVISOR", np.float32(448.0))
+    assert _fails(PQ.test_amax_block_takes_the_largest_scale_and_code)
+    assert _fails(PQ.test_hand_worked_example, golden_dir)
+
+
+def test_ties_away_from_even_are_caught(monkeypatch):
+    def away(aq):
+        a = np.asarray(aq, dtype=np.float32)
+        conds = [a < 0.25, a < 0.75, a < 1.25, a < 1.75, a < 2.5, a < 3.5, a < 5.0]
+        return np.select(conds, [0, 1, 2, 3, 4, 5, 6], default=7).astype(np.uint8)
+    monkeypatch.setattr(OM, "e2m1_encode_magnitude", away)
+    assert _fails(PQ.test_brute_force_midpoint_ties)
+
+
+def test_dropped_rank_term_is_caught(monkeypatch):
+    orig = OM.reconstruct
+
+    def dropped(W0, s=None, U=None, V=None):
+        if U is None:
+            return orig(W0, s)
+        return orig(W0, s, U[:, :-1], V[:, :-1])
+    monkeypatch.setattr(OM, "reconstruct", dropped)
+    monkeypatch.setattr(O, "reconstruct", dropped)
+    assert _fails(PR.test_exact_small_integer_lowrank_matches_rational_value)
+
+
+def test_transposed_factor_is_caught(monkeypatch):
+    orig = OM.reconstruct
+
+    def swapped(W0, s=None, U=None, V=None):
+        if U is None:
+            return orig(W0, s)
+        # V indexed by row instead of column: only defined when reading V[:N]
+        N = W0.shape[0]
+        K = W0.shape[1]
+        Vw = np.resize(V[:N][::-1], (K, V.shape[1]))
+        return orig(W0, s, U, Vw)
+    monkeypatch.setattr(OM, "reconstruct", swapped)
+    monkeypatch.setattr(O, "reconstruct", swapped)
+    assert _fails(PR.test_exact_small_integer_lowrank_matches_rational_value)
+
+
+def test_scale_applied_to_wrong_rows_is_caught(monkeypatch):
+    orig = OM.row_segment_scale
+
+    def shifted(N, seg_end, ts):
+        return orig(N, seg_end, np.roll(np.asarray(ts), 1))
+    monkeypatch.setattr(OM, "row_segment_scale", shifted)
+    assert _fails(PG.test_gemv_equals_exact_rational_sum)
+
+
+def test_gemv_sign_slip_is_caught(monkeypatch):
+    orig = OM.e2m1_decode
+
+    def nosign(codes):
+        return np.abs(orig(codes))
+    monkeypatch.setattr(OM, "e2m1_decode", nosign)
+    assert _fails(PG.test_gemv_equals_exact_rational_sum)
+
+
+def test_dropped_block_is_caught(monkeypatch):
+    orig = OM.unpack_codes
+
+    def drop_last_block(codes):
+        out = orig(codes).copy()
+        out[..., -16:] = 0
+        return out
+    monkeypatch.setattr(OM, "unpack_codes", drop_last_block)
+    assert _fails(PG.test_gemv_equals_exact_rational_sum)
