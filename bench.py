@@ -1,0 +1,386 @@
+"""Benchmark: NVFP4 weight streaming for batch-1 decode of a 31B-like model on one MI355X.
+
+One step = one token of the whole-model weight stream: 60 layers x {fused q|k|v 6144x5376,
+o 5376x4096, fused gate|up 43008x5376, down 5376x21504} NVFP4 GEMVs plus the tied bf16
+lm_head 262144x5376 GEMV -- 241 kernel launches, replayed as one hipGraph. Every layer has
+its own weights (16.4 GB per token, far above the 256 MB last-level cache), already resident
+in HBM when timing starts.
+
+The weights are built on the GPU by the load path itself: seeded bf16 W0 drawn on the device,
+then attnq_quantize_nvfp4 (passthrough reconstruction). The load path is also timed on its
+own workload -- all 410 theta bundles at rank 16 with s ~ U(0.9, 1.1) (420 segment
+quantizations: in 10 layers k's bundle also fills the v rows) -- and so is the small-M verify
+product (M = 4 and 8) on one layer; both are reported as extra fields.
+
+Output: one JSON line (see the design doc for the fields). Options:
+  --steps K --warmup W       timed / untimed steps (defaults 20 / 5)
+  --gpus N                   only N = 1 is supported (one GPU)
+  --no-cpu-baseline          skip the oracle timing
+  --no-load-path             skip the rank-16 load-path timing (saves ~48 GB of W0)
+  --eager                    time plain stream launches instead of the hipGraph replay
+  --calibrate-copy           also run a 1 GiB device copy (for counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HIDDEN = 5376
+N_LAYERS = 60
+QKV_SEGS = (4096, 1024, 1024)
+O_SHAPE = (HIDDEN, 4096)
+GU_SEGS = (21504, 21504)
+DOWN_SHAPE = (HIDDEN, 21504)
+VOCAB = 262144
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+VALU_FP32_PEAK_TFLOPS = 157.3  # published fp32 vector peak (packed), for the load path note
+PROJ_NAMES = ("qkv", "o", "gate_up", "down")
+
+
+def nvfp4_bytes(N: int, K: int, n_seg: int) -> int:
+    """Algorithmic HBM bytes of one NVFP4 GEMV: codes + scales + tensor scales + x + y."""
+    return N * K // 2 + N * K // 16 + 4 * n_seg + 2 * K + 4 * N
+
+
+def bf16_bytes(N: int, K: int) -> int:
+    return 2 * N * K + 2 * K + 4 * N
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Model:
+    """Device-resident NVFP4 weights of the 31B-like stack plus per-projection x / y buffers."""
+
+    def __init__(self, A, dev):
+        self.A = A
+        self.layers = []
+        seed = 1000
+        for L in range(N_LAYERS):
+            lay = {}
+            for name, segs, K in (("qkv", QKV_SEGS, HIDDEN), ("o", (O_SHAPE[0],), O_SHAPE[1]),
+                                  ("gate_up", GU_SEGS, HIDDEN), ("down", (DOWN_SHAPE[0],), DOWN_SHAPE[1])):
+                N = sum(segs)
+                ends = list(np.cumsum(segs))
+                W = A.NVFP4Weight.empty(N, K, ends, device=dev)
+                x = torch.randn(K, device=dev, generator=torch.Generator(device=dev).manual_seed(seed)).to(torch.bfloat16)
+                seed += 1
+                y = torch.empty(N, dtype=torch.float32, device=dev)
+                lay[name] = (W, x, y, segs, K)
+            self.layers.append(lay)
+        from nvfp4_weight_only_rtn_amd import inputs
+        self.lm_head = inputs.device_normal_bf16((VOCAB, HIDDEN), 0.02, seed=7, device=dev)
+        self.x_head = torch.randn(HIDDEN, device=dev, generator=torch.Generator(device=dev).manual_seed(8)).to(torch.bfloat16)
+        self.y_head = torch.empty(VOCAB, dtype=torch.float32, device=dev)
+
+    def quantize_passthrough(self, dev):
+        """Fill every NVFP4 weight from a seeded device bf16 W0 (passthrough reconstruction)."""
+        from nvfp4_weight_only_rtn_amd import inputs
+        seed = 50_000
+        for lay in self.layers:
+            for name in PROJ_NAMES:
+                W, _, _, segs, K = lay[name]
+                for i, n in enumerate(segs):
+                    W0 = inputs.device_normal_bf16((n, K), 0.02, seed=seed, device=dev)
+                    seed += 1
+                    self.A.attnq_quantize_nvfp4(W0, None, None, None, W, seg=i)
+        torch.cuda.synchronize()
+
+    def step(self):
+        A = self.A
+        for lay in self.layers:
+            for name in PROJ_NAMES:
+                W, x, y, _, _ = lay[name]
+                A.attnq_gemv_nvfp4(W, x, y)
+        A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
+
+    def bytes_per_step(self) -> int:
+        total = 0
+        for lay in self.layers:
+            for name in PROJ_NAMES:
+                W, _, _, segs, K = lay[name]
+                total += nvfp4_bytes(W.N, K, len(segs))
+        return total + bf16_bytes(VOCAB, HIDDEN)
+
+    def weight_bytes_per_step(self) -> int:
+        total = sum(lay[n][0].nbytes for lay in self.layers for n in PROJ_NAMES)
+        return total + 2 * VOCAB * HIDDEN
+
+
+def time_steps(fn, steps: int) -> float:
+    """ms per step over exactly `steps` calls, bracketed by device synchronization."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def dominant_kernel_timing(model: Model, steps: int):
+    """Average duration of the gate|up NVFP4 GEMV launches (the largest byte share of a token),
+    measured with HIP events on the launch stream around each launch of eager steps."""
+    A = model.A
+    pairs = []
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        for lay in model.layers:
+            for name in PROJ_NAMES:
+                W, x, y, _, _ = lay[name]
+                if name == "gate_up":
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    A.attnq_gemv_nvfp4(W, x, y)
+                    e1.record()
+                    pairs.append((e0, e1))
+                else:
+                    A.attnq_gemv_nvfp4(W, x, y)
+        A.attnq_gemv_bf16(model.lm_head, model.x_head, model.y_head)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in pairs]
+    return float(np.mean(ms)), float(np.median(ms)), len(ms)
+
+
+def load_path_timing(A, dev, model: Model, reps: int = 1):
+    """Rank-16 reconstruct + RTN quantize over all 410 theta bundles (420 segment writes)."""
+    from nvfp4_weight_only_rtn_amd import inputs
+    r = 16
+    bundles = []      # (W, seg, W0, s, U, V)
+    seed = 900_000
+    elements = 0
+    distinct = 0
+    for L, lay in enumerate(model.layers):
+        for name in PROJ_NAMES:
+            W, _, _, segs, K = lay[name]
+            prev = None
+            for i, n in enumerate(segs):
+                reuse_k_for_v = name == "qkv" and i == 2 and L % 6 == 5     # 10 layers without a v bundle
+                if reuse_k_for_v:
+                    W0, s, U, V = prev
+                else:
+                    W0 = inputs.device_normal_bf16((n, K), 0.02, seed=seed, device=dev)
+                    s = inputs.device_uniform_bf16((n,), 0.9, 1.1, seed=seed + 1, device=dev)
+                    U = inputs.device_normal_bf16((n, r), 1e-3, seed=seed + 2, device=dev)
+                    V = inputs.device_normal_bf16((K, r), 1e-3, seed=seed + 3, device=dev)
+                    seed += 4
+                    distinct += 1
+                prev = (W0, s, U, V)
+                bundles.append((W, i, W0, s, U, V))
+                elements += n * K
+    torch.cuda.synchronize()
+
+    def run():
+        for (W, i, W0, s, U, V) in bundles:
+            A.attnq_quantize_nvfp4(W0, s, U, V, W, seg=i)
+    run()                                   # warm-up (first-touch of every buffer)
+    ms = time_steps(run, reps)
+    del bundles
+    torch.cuda.empty_cache()
+    return ms, elements, distinct
+
+
+def small_m_timing(A, model: Model, steps: int):
+    """M = 4 (gamma 3 + 1) and M = 8 verify products over one layer's four projections."""
+    out = {}
+    lay = model.layers[0]
+    for M in (4, 8):
+        bufs = []
+        nbytes = 0
+        flops = 0
+        for name in PROJ_NAMES:
+            W, _, _, segs, K = lay[name]
+            X = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+            Y = torch.empty((M, W.N), dtype=torch.float32, device="cuda")
+            bufs.append((W, X, Y))
+            nbytes += W.nbytes + 2 * M * K + 4 * M * W.N
+            flops += 2 * M * W.N * K
+
+        def run():
+            for (W, X, Y) in bufs:
+                A.attnq_gemm_nvfp4_small_m(W, X, Y)
+        run()
+        # one layer (226 MB) fits the 256 MB last-level cache; time it cold by walking 8 layers
+        bufs_all = []
+        for L in range(8):
+            for name in PROJ_NAMES:
+                W, _, _, segs, K = model.layers[L][name]
+                bufs_all.append((W, bufs[PROJ_NAMES.index(name)][1], bufs[PROJ_NAMES.index(name)][2]))
+
+        def run8():
+            for (W, X, Y) in bufs_all:
+                A.attnq_gemm_nvfp4_small_m(W, X, Y)
+        run8()
+        ms = time_steps(run8, steps) / 8
+        out[f"M{M}"] = {"us_per_layer": round(ms * 1e3, 2), "TBps": round(nbytes / (ms * 1e-3) / 1e12, 3),
+                        "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2)}
+    return out
+
+
+def cpu_baseline():
+    """The oracle's dequantize + float64 GEMV on a bounded sample: the fused q|k|v and the o
+    projection of one 31B-like layer (55.1 M weights, 31.0 MB NVFP4)."""
+    import oracle as O
+    from nvfp4_weight_only_rtn_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    work = []
+    for name, segs, K in (("qkv", QKV_SEGS, HIDDEN), ("o", (O_SHAPE[0],), O_SHAPE[1])):
+        bundles = [inputs.theta_bundle(n, K, 0, cfg=2, layer=0, proj=p, passthrough=True) for p, n in enumerate(segs)]
+        parts = [O.quantize_segment(b[0]) for b in bundles]
+        codes = np.concatenate([p[0] for p in parts])
+        scales = np.concatenate([p[1] for p in parts])
+        ts = np.array([p[2] for p in parts], dtype=np.float32)
+        x = inputs.activation_bf16(1, K, 2, 0, 0)
+        work.append((codes, scales, ts, list(np.cumsum(segs)), x))
+    nbytes = sum(c.nbytes + s.nbytes + t.nbytes for c, s, t, _, _ in work)
+    t0 = time.perf_counter()
+    for codes, scales, ts, ends, x in work:
+        O.gemv_nvfp4(codes, scales, ts, x, ends)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e12, 9), "unit": "TB/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"oracle dequantize + float64 GEMV of the fused q|k|v (6144x5376) and o (5376x4096) "
+                      f"projections of one 31B-like layer: {nbytes} NVFP4 bytes in {dt:.2f} s "
+                      f"(numpy elementwise on 1 thread, BLAS on {blas}; affinity {len(os.sched_getaffinity(0))} cpus)"}
+
+
+def calibrate_copy(dev):
+    """1 GiB device-to-device copy, a kernel of known traffic for counter calibration."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"calibration copy: 3 x {n} bytes read and written")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-load-path", action="store_true")
+    ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the weight stream is a single-device path "
+              "(more GPUs would shard rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import nvfp4_weight_only_rtn_amd.attnq as A
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log("allocating the 31B-like stack")
+    model = Model(A, dev)
+    log("loading weights (device W0 -> attnq_quantize_nvfp4, passthrough)")
+    t0 = time.perf_counter()
+    model.quantize_passthrough(dev)
+    log(f"passthrough load {time.perf_counter() - t0:.1f} s")
+
+    load = None
+    if not args.no_load_path:
+        log("timing the rank-16 load path over 410 bundles")
+        ms, elements, distinct = load_path_timing(A, dev, model)
+        # 4.5625 B per element: W0 read twice (amax pass, quantize pass) + 0.5625 B written
+        nbytes = int(elements * 4.5625)
+        flops = elements * 2 * 16 * 2
+        load = {"ms": round(ms, 3), "elements": elements, "bundles": distinct, "segments": 420,
+                "TBps_algorithmic": round(nbytes / (ms * 1e-3) / 1e12, 3),
+                "fma_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2)}
+        log(f"load path: {load}")
+        model.quantize_passthrough(dev)   # restore the passthrough weights for the stream
+
+    for _ in range(args.warmup):
+        model.step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.eager:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            model.step()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            model.step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = model.step
+    for _ in range(args.warmup):
+        run()
+    ms = time_steps(run, args.steps)
+    eager_ms = time_steps(model.step, max(3, args.steps // 4))
+    bytes_step = model.bytes_per_step()
+    tbps = bytes_step / (ms * 1e-3) / 1e12
+    log(f"{'graph' if graph else 'eager'} {ms:.4f} ms/token, eager {eager_ms:.4f} ms/token, {tbps:.3f} TB/s")
+
+    dom_mean, dom_median, dom_n = dominant_kernel_timing(model, max(2, args.steps // 4))
+    W_gu = model.layers[0]["gate_up"][0]
+    dom_bytes = nvfp4_bytes(W_gu.N, W_gu.K, 2)
+    achieved = dom_bytes / (dom_mean * 1e-3) / 1e9
+
+    small_m = small_m_timing(A, model, max(3, args.steps // 4))
+    if args.calibrate_copy:
+        calibrate_copy(dev)
+
+    out = {
+        "metric": "NVFP4 GEMV achieved HBM TB/s (% of peak) + ms per token weight stream, 31B-like",
+        "value": round(tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 weights (e2m1 + e4m3 block scales) x bf16 activations, fp32 accumulate",
+        "data": "synthetic: seeded device bf16 W0 ~ N(0, 0.02^2) RTN-quantized by the library at load; x ~ N(0, 1)",
+        "config": {"workload": "31B-like whole-model weight stream per token: 60 layers x (q|k|v 6144x5376, "
+                               "o 5376x4096, gate|up 43008x5376, down 5376x21504) NVFP4 + bf16 lm_head 262144x5376, batch 1",
+                   "launches_per_step": 4 * N_LAYERS + 1, "launch": "hipGraph replay" if graph else "stream",
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * tbps * 1e3 / HBM_PEAK_GBS, 2),
+        "ms_per_token": round(ms, 5),
+        "ms_per_token_eager": round(eager_ms, 5),
+        "bytes_per_token": bytes_step,
+        "weight_bytes_per_token": model.weight_bytes_per_step(),
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4<4,1> (fused gate|up 43008x5376)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_mean * 1e3, 3),
+                     "median_launch_us": round(dom_median * 1e3, 3), "launches_timed": dom_n},
+        "small_m": small_m,
+        "load_path": load,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

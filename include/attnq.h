@@ -1,0 +1,150 @@
+/*
+ * attnq.h -- C ABI of libattnq.so: load-time NVFP4 weight-only RTN quantization and the
+ * batch-1 / tiny-batch decode projections y = x * W_eff^T on AMD Instinct MI355X (gfx950).
+ *
+ * Source of the operations (documentation pages of the AttnQuant / weightless projects):
+ *   - theta bundle and reconstruction W_eff = s*W0 + U*V^T: AttnQuant landing page,
+ *     "How it works"; weightless "GPU and cache acceleration", "Architecture decisions /
+ *     Precompute-outside (the fast path)".
+ *   - NVFP4 round-to-nearest quantization at load, packed uint8 codes plus float8 block
+ *     scales: "GPU acceleration", "NVFP4 quantization"; landing page, "Results";
+ *     "Throughput", "What quantization actually saves" (one float8_e4m3fn scale per 16
+ *     elements, 0.5625 B per element).
+ *   - the decode GEMVs that consume fp4 directly with no dequant pass, fused Q/K/V, the bf16
+ *     tied lm_head: "GPU acceleration", "Where GPU time goes" and "Q/K/V fusion";
+ *     "Throughput", "The NVFP4 MLP kernels are the least bandwidth-efficient on the step".
+ *   - small-M products for speculative verification (gamma = 3 drafts plus one) and batch 8:
+ *     "Throughput", "Speculative decoding".
+ *
+ * Conventions shared by every call:
+ *   - Memory: every array argument is DEVICE memory owned by the caller; descriptor structs
+ *     are HOST memory read during the call only. The library allocates nothing and keeps no
+ *     mutable global state, so calls from several host threads are safe.
+ *   - Asynchrony: each call validates its arguments on the host, enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL is the default stream) and returns. It never
+ *     synchronizes, copies to or from the host, or reads device data on the host.
+ *   - Errors: argument errors are returned synchronously before anything is enqueued; a
+ *     failed launch returns ATTNQ_ERR_HIP. Bad data is reported in-band: a projection whose
+ *     weights hold a NaN or an infinity gets tensor scale NaN, so its outputs are NaN.
+ *   - bf16 values travel as uint16_t bit patterns; outputs y / Y are fp32.
+ *   - Shapes: K must be a positive multiple of 32 (two scale blocks per 16-byte code chunk);
+ *     N == 0 (or M == 0) is a valid no-op, and a pointer to such an empty array may be NULL.
+ */
+#ifndef ATTNQ_H
+#define ATTNQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported entry points (the library is built with hidden default visibility). */
+#define ATTNQ_API __attribute__((visibility("default")))
+
+typedef enum attnq_status {
+  ATTNQ_OK = 0,
+  ATTNQ_ERR_NULL = 1,    /* a required pointer is NULL */
+  ATTNQ_ERR_SHAPE = 2,   /* a size is out of range (see each call) */
+  ATTNQ_ERR_ALIGN = 3,   /* a device pointer is not aligned as documented */
+  ATTNQ_ERR_SEGMENT = 4, /* segment table or segment index inconsistent */
+  ATTNQ_ERR_LAYOUT = 5,  /* unknown packed-weight layout id */
+  ATTNQ_ERR_HIP = 6      /* a kernel launch failed */
+} attnq_status;
+
+/* hipStream_t, passed opaquely so that this header needs no HIP include. */
+typedef void* attnq_stream;
+
+/* One projection's theta bundle (landing page, "How it works").
+ *   W0 [N][K] bf16 row-major, 16-byte aligned. Several bundles may point at one W0
+ *      (a shared block).
+ *   s  [N] bf16 per-row scale, or NULL for s = 1.
+ *   U  [N][r] bf16, V [K][r] bf16 (row-major), both NULL iff r == 0; 0 <= r <= 64.
+ * A plain bf16 weight W is the bundle {W, NULL, NULL, NULL, N, K, 0}. */
+typedef struct attnq_theta {
+  const uint16_t* W0;
+  const uint16_t* s;
+  const uint16_t* U;
+  const uint16_t* V;
+  int32_t N;
+  int32_t K;
+  int32_t r;
+} attnq_theta;
+
+#define ATTNQ_MAX_SEGMENTS 4
+#define ATTNQ_LAYOUT_ROW_MAJOR 0
+
+/* An NVFP4 weight [N][K], possibly several projections fused along N ("Q/K/V fusion":
+ * q, k, v rows concatenated; gate and up likewise). Segment i covers rows
+ * [seg_end[i-1], seg_end[i]) (seg_end[-1] = 0) and has its own tensor scale.
+ *   codes  [N][K/2] u8, 16-byte aligned: element 2j of a row in the low nibble of byte j,
+ *          element 2j+1 in the high nibble; a nibble is sign<<3 | E2M1 magnitude index
+ *          (0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *   scales [N][K/16] E4M3FN, 4-byte aligned: block b scales elements [16b, 16b+16) of a row.
+ *   tensor_scale [n_seg] fp32, 4-byte aligned: the dequantization multiplier of a segment.
+ *   weight[n][k] = e2m1(code) * e4m3(scale[n][k/16]) * tensor_scale[segment of n].
+ *   1 <= n_seg <= 4, seg_end strictly ascending, seg_end[n_seg-1] == N.
+ *   layout: ATTNQ_LAYOUT_ROW_MAJOR (0) is the only layout. */
+typedef struct attnq_nvfp4 {
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tensor_scale;
+  int32_t N;
+  int32_t K;
+  int32_t n_seg;
+  int32_t seg_end[ATTNQ_MAX_SEGMENTS];
+  int32_t layout;
+} attnq_nvfp4;
+
+/* W_eff = s*W0 + U*V^T (landing page "How it works"; weightless "Precompute-outside").
+ * Rounding: acc = 0, acc += U[i][k]*V[j][k] in fp32 for k ascending, w = s_i*W0[i][j] + acc
+ * (skipped add when r == 0), one fp32 rounding per step, then bf16 round-to-nearest-even.
+ * With s = NULL and r = 0 the output equals W0 bit for bit.
+ * W_eff [N][K] bf16, 16-byte aligned, must not overlap the inputs.
+ * Errors: NULL theta/W0/W_eff or (r > 0 and NULL U/V); N < 0, K not a positive multiple of
+ * 32, r outside [0, 64]; misaligned W0 / W_eff. */
+ATTNQ_API attnq_status attnq_reconstruct(const attnq_theta* theta, uint16_t* W_eff, attnq_stream stream);
+
+/* Reconstruct (as attnq_reconstruct, in registers) and round-to-nearest quantize one
+ * projection into segment `seg` of `dst` ("NVFP4 quantization"; landing page "Results").
+ * Per segment: amax = max |W_eff|; ts = fl32(amax / 2688) (2688 = 6 * 448);
+ * per 16-element block: S = E4M3(fl32(bamax / fl32(6*ts))) rounded to nearest, ties to even,
+ * saturating at 448; d = fl32(e4m3(S)*ts); each element: q = fl32(w / d) rounded to the E2M1
+ * grid, ties to the even code, saturating at 6, sign of w kept; S == 0 gives magnitude 0.
+ * amax == 0 gives ts = 0 and all scales 0. A NaN/inf in the segment gives ts = NaN, every
+ * scale 0x7F and every code byte 0.
+ * theta->N must equal the segment's row count and theta->K == dst->K. The segment's
+ * tensor_scale slot is used as the amax accumulator while the call runs (four kernels in
+ * stream order); other segments of dst are untouched.
+ * Errors: as attnq_reconstruct, plus ATTNQ_ERR_SEGMENT for a bad seg or row count and
+ * ATTNQ_ERR_LAYOUT for an unknown layout. */
+ATTNQ_API attnq_status attnq_quantize_nvfp4(const attnq_theta* theta, const attnq_nvfp4* dst, int32_t seg,
+                                  attnq_stream stream);
+
+/* y[n] = sum_k x[k] * weight[n][k] for an NVFP4 weight: one kernel that reads codes and
+ * scales once and decodes fp4 in registers ("Where GPU time goes": no dequant pass).
+ * x [K] bf16 16-byte aligned; y [N] fp32 4-byte aligned, must not overlap x or the weight.
+ * Accumulation is fp32. */
+ATTNQ_API attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y,
+                              attnq_stream stream);
+
+/* y[n] = sum_k x[k] * W[n][k] for a bf16 weight [N][K] (the tied lm_head, or projections
+ * left in bf16). W and x 16-byte aligned, y 4-byte aligned. fp32 accumulation. */
+ATTNQ_API attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, const uint16_t* x, float* y,
+                             attnq_stream stream);
+
+/* Y[m][n] = sum_k X[m][k] * weight[n][k] for 0 <= M <= 16 token rows (speculative verify at
+ * gamma + 1 = 4, batch 8). X row m at X + m*ldx (bf16, ldx >= K, ldx % 8 == 0, X 16-byte
+ * aligned); Y row m at Y + m*ldy (fp32, ldy >= N, Y 4-byte aligned). Uses MFMA matrix cores;
+ * fp32 accumulation. */
+ATTNQ_API attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, int32_t M,
+                                      int32_t ldx, float* Y, int32_t ldy, attnq_stream stream);
+
+/* Static string naming a status code (host only). */
+ATTNQ_API const char* attnq_status_string(attnq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNQ_H */

@@ -1,0 +1,111 @@
+// C ABI of libattnq.so: host-side argument validation, then the kernel launchers.
+// Validation touches no device memory and makes no HIP call, so every error path below can
+// be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attnq.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int32_t kMaxRank = 64;
+constexpr int32_t kMaxM = 16;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// A pointer to an empty array (N == 0) may be NULL; everything else must be non-NULL.
+attnq_status check_theta(const attnq_theta* t) {
+  if (t == nullptr) return ATTNQ_ERR_NULL;
+  if (t->W0 == nullptr && t->N != 0) return ATTNQ_ERR_NULL;
+  if (t->N < 0 || t->K <= 0 || t->K % 32 != 0 || t->r < 0 || t->r > kMaxRank) return ATTNQ_ERR_SHAPE;
+  if (t->r > 0 && (t->U == nullptr || t->V == nullptr)) return ATTNQ_ERR_NULL;
+  if (!aligned(t->W0, 16)) return ATTNQ_ERR_ALIGN;
+  if (t->s && !aligned(t->s, 2)) return ATTNQ_ERR_ALIGN;
+  if (t->r > 0 && (!aligned(t->U, 2) || !aligned(t->V, 2))) return ATTNQ_ERR_ALIGN;
+  return ATTNQ_OK;
+}
+
+attnq_status check_nvfp4(const attnq_nvfp4* w) {
+  if (w == nullptr || w->tensor_scale == nullptr) return ATTNQ_ERR_NULL;
+  if ((w->codes == nullptr || w->scales == nullptr) && w->N != 0) return ATTNQ_ERR_NULL;
+  if (w->layout != ATTNQ_LAYOUT_ROW_MAJOR) return ATTNQ_ERR_LAYOUT;
+  if (w->N < 0 || w->K <= 0 || w->K % 32 != 0) return ATTNQ_ERR_SHAPE;
+  if (w->n_seg < 1 || w->n_seg > ATTNQ_MAX_SEGMENTS) return ATTNQ_ERR_SEGMENT;
+  int32_t prev = 0;
+  for (int i = 0; i < w->n_seg; ++i) {
+    if (w->seg_end[i] <= prev && !(w->N == 0 && w->n_seg == 1)) return ATTNQ_ERR_SEGMENT;
+    prev = w->seg_end[i];
+  }
+  if (w->seg_end[w->n_seg - 1] != w->N) return ATTNQ_ERR_SEGMENT;
+  if (!aligned(w->codes, 16) || !aligned(w->scales, 4) || !aligned(w->tensor_scale, 4)) return ATTNQ_ERR_ALIGN;
+  return ATTNQ_OK;
+}
+
+attnq_status from_hip(hipError_t e) { return e == hipSuccess ? ATTNQ_OK : ATTNQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+attnq_status attnq_reconstruct(const attnq_theta* theta, uint16_t* W_eff, attnq_stream stream) {
+  attnq_status st = check_theta(theta);
+  if (st != ATTNQ_OK) return st;
+  if (W_eff == nullptr && theta->N != 0) return ATTNQ_ERR_NULL;
+  if (!aligned(W_eff, 16)) return ATTNQ_ERR_ALIGN;
+  return from_hip(attnq::launch_reconstruct(*theta, W_eff, static_cast<hipStream_t>(stream)));
+}
+
+attnq_status attnq_quantize_nvfp4(const attnq_theta* theta, const attnq_nvfp4* dst, int32_t seg, attnq_stream stream) {
+  attnq_status st = check_theta(theta);
+  if (st != ATTNQ_OK) return st;
+  st = check_nvfp4(dst);
+  if (st != ATTNQ_OK) return st;
+  if (theta->K != dst->K) return ATTNQ_ERR_SHAPE;
+  if (seg < 0 || seg >= dst->n_seg) return ATTNQ_ERR_SEGMENT;
+  const int32_t start = seg == 0 ? 0 : dst->seg_end[seg - 1];
+  if (dst->seg_end[seg] - start != theta->N) return ATTNQ_ERR_SEGMENT;
+  uint8_t* codes = dst->codes + (size_t)start * (dst->K / 2);
+  uint8_t* scales = dst->scales + (size_t)start * (dst->K / 16);
+  return from_hip(attnq::launch_quantize(*theta, codes, scales, dst->tensor_scale + seg, static_cast<hipStream_t>(stream)));
+}
+
+attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y, attnq_stream stream) {
+  attnq_status st = check_nvfp4(W);
+  if (st != ATTNQ_OK) return st;
+  if (x == nullptr || (y == nullptr && W->N != 0)) return ATTNQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 4)) return ATTNQ_ERR_ALIGN;
+  return from_hip(attnq::launch_gemv_nvfp4(*W, x, y, static_cast<hipStream_t>(stream)));
+}
+
+attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, const uint16_t* x, float* y, attnq_stream stream) {
+  if (N < 0 || K <= 0 || K % 32 != 0) return ATTNQ_ERR_SHAPE;
+  if (x == nullptr || ((W == nullptr || y == nullptr) && N != 0)) return ATTNQ_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return ATTNQ_ERR_ALIGN;
+  return from_hip(attnq::launch_gemv_bf16(W, N, K, x, y, static_cast<hipStream_t>(stream)));
+}
+
+attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, int32_t M, int32_t ldx, float* Y,
+                                      int32_t ldy, attnq_stream stream) {
+  attnq_status st = check_nvfp4(W);
+  if (st != ATTNQ_OK) return st;
+  if (M < 0 || M > kMaxM || ldx < W->K || ldx % 8 != 0 || ldy < W->N) return ATTNQ_ERR_SHAPE;
+  if ((X == nullptr || Y == nullptr) && M != 0 && W->N != 0) return ATTNQ_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(Y, 4)) return ATTNQ_ERR_ALIGN;
+  return from_hip(attnq::launch_gemm_nvfp4_small_m(*W, X, M, ldx, Y, ldy, static_cast<hipStream_t>(stream)));
+}
+
+const char* attnq_status_string(attnq_status status) {
+  switch (status) {
+    case ATTNQ_OK: return "ATTNQ_OK";
+    case ATTNQ_ERR_NULL: return "ATTNQ_ERR_NULL: a required pointer is NULL";
+    case ATTNQ_ERR_SHAPE: return "ATTNQ_ERR_SHAPE: a size is out of range";
+    case ATTNQ_ERR_ALIGN: return "ATTNQ_ERR_ALIGN: a device pointer is misaligned";
+    case ATTNQ_ERR_SEGMENT: return "ATTNQ_ERR_SEGMENT: segment table or index inconsistent";
+    case ATTNQ_ERR_LAYOUT: return "ATTNQ_ERR_LAYOUT: unknown packed-weight layout";
+    case ATTNQ_ERR_HIP: return "ATTNQ_ERR_HIP: a kernel launch failed";
+  }
+  return "attnq: unknown status";
+}
+
+}  // extern "C"

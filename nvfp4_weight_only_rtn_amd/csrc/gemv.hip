@@ -1,0 +1,196 @@
+// Decode GEMVs y = x * W^T at batch 1: the NVFP4 weight-streaming kernel and the bf16 one.
+//
+// "GPU acceleration", "Where GPU time goes": batch-1 decode is dominated by GEMVs that read
+// every weight once, and the block-scaled kernel consumes fp4 directly (no dequant launch).
+// "Throughput", "The NVFP4 MLP kernels are the least bandwidth-efficient on the step": the
+// B200 kernels reach 47% (NVFP4) and 57-65% (bf16) of HBM peak; the down projection ran
+// short of parallelism (42 CTAs on 148 SMs), hence the K split below for long rows.
+//
+// Mapping (gfx950, wave64): a lane owns one 16-byte code chunk (32 fp4 = two scale blocks) of
+// R rows per step, so each wave load instruction covers 1 KiB of one row, fully coalesced;
+// the 64 B of x for that chunk are loaded once and reused for the R rows. Decode is
+// v_cvt_scalef32_pk_bf16_fp4 (two fp4 -> two bf16, exact, scale 1) feeding v_dot2c_f32_bf16
+// into a per-block fp32 partial, which is multiplied by its E4M3 scale once per block. Wave
+// partials are reduced with DPP; with a K split, the waves of a workgroup meet in LDS.
+#include "attnq_device.h"
+#include "launch.h"
+
+namespace attnq {
+
+namespace {
+
+// One scale block: 16 fp4 (two dwords of codes) against 16 bf16 of x (eight dwords).
+__device__ __forceinline__ float dot16_fp4(uint32_t codes_lo, uint32_t codes_hi, const uint32_t* xw) {
+  float p = 0.0f;
+  p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes_lo, 1.0f, 0),
+                                      as_bf16x2(xw[0]), p, false);
+  p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes_lo, 1.0f, 1),
+                                      as_bf16x2(xw[1]), p, false);
+  p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes_lo, 1.0f, 2),
+                                      as_bf16x2(xw[2]), p, false);
+  p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes_lo, 1.0f, 3),
+                                      as_bf16x2(xw[3]), p, false);
+  p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes_hi, 1.0f, 0),
+                                      as_bf16x2(xw[4]), p, false);
+  p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes_hi, 1.0f, 1),
+                                      as_bf16x2(xw[5]), p, false);
+  p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes_hi, 1.0f, 2),
+                                      as_bf16x2(xw[6]), p, false);
+  p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes_hi, 1.0f, 3),
+                                      as_bf16x2(xw[7]), p, false);
+  return p;
+}
+
+// One 16-byte chunk of one row: two blocks, each partial scaled by its E4M3 scale.
+__device__ __forceinline__ float chunk_dot(const u32x4 cv, uint32_t sv, const uint32_t* xw, float acc) {
+  const float p0 = dot16_fp4(cv.x, cv.y, xw);
+  const float p1 = dot16_fp4(cv.z, cv.w, xw + 8);
+  acc = __builtin_fmaf(p0, __builtin_amdgcn_cvt_f32_fp8((int)sv, 0), acc);
+  acc = __builtin_fmaf(p1, __builtin_amdgcn_cvt_f32_fp8((int)sv, 1), acc);
+  return acc;
+}
+
+template <int R, int KSPLIT>
+__global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                    const float* __restrict__ tensor_scale, SegTable segs,
+                                                    const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K) {
+  static_assert(4 % KSPLIT == 0, "K split must divide the 4 waves of a workgroup");
+  constexpr int kRowGroups = 4 / KSPLIT;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rg = wave / KSPLIT, ks = wave % KSPLIT;
+  const int row0 = (blockIdx.x * kRowGroups + rg) * R;
+  const int cpr = K >> 5;
+  const int slice = (cpr + KSPLIT - 1) / KSPLIT;
+  const int c_begin = ks * slice;
+  const int c_end = min(cpr, c_begin + slice);
+  const size_t code_pitch = (size_t)K >> 1;
+  const size_t scale_pitch = (size_t)K >> 4;
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+  for (int c = c_begin + lane; c < c_end; c += 64) {
+    const u32x4* xp = reinterpret_cast<const u32x4*>(x + (size_t)c * kChunkElems);
+    const u32x4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+    const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                             x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+    u32x4 cv[R];
+    uint32_t sv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(row0 + r, N - 1);          // clamp: rows past N load row N-1, result discarded
+      cv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + row * code_pitch) + c);
+      sv[r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = chunk_dot(cv[r], sv[r], xw, acc[r]);
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+
+  if constexpr (KSPLIT == 1) {
+    if (lane < R) {
+      float v = acc[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
+      const int row = row0 + lane;
+      if (row < N) y[row] = v * tensor_scale[segment_of(segs, row)];
+    }
+  } else {
+    __shared__ float part[4][R];
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[wave][r] = acc[r];
+    }
+    __syncthreads();
+    if (ks == 0 && lane < R) {
+      float v = 0.0f;
+#pragma unroll
+      for (int s = 0; s < KSPLIT; ++s) v += part[wave + s][lane];
+      const int row = row0 + lane;
+      if (row < N) y[row] = v * tensor_scale[segment_of(segs, row)];
+    }
+  }
+}
+
+// bf16 weights: a lane owns one 16-byte chunk (8 bf16) of R rows per step; x chunk reused.
+template <int R>
+__global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
+                                                   float* __restrict__ y, int N, int K) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * 4 + wave) * R;
+  const int cpr = K >> 3;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int c = lane; c < cpr; c += 64) {
+    const u32x4 xv = reinterpret_cast<const u32x4*>(x)[c];
+    u32x4 wv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(row0 + r, N - 1);
+      wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)row * K) + c);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float a = acc[r];
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[r].x), as_bf16x2(xv.x), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[r].y), as_bf16x2(xv.y), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[r].z), as_bf16x2(xv.z), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[r].w), as_bf16x2(xv.w), a, false);
+      acc[r] = a;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane < R) {
+    float v = acc[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
+    const int row = row0 + lane;
+    if (row < N) y[row] = v;
+  }
+}
+
+SegTable seg_table(const attnq_nvfp4& W) {
+  SegTable t;
+  t.n_seg = W.n_seg;
+  for (int i = 0; i < ATTNQ_MAX_SEGMENTS; ++i) t.end[i] = (i < W.n_seg) ? W.seg_end[i] : W.N;
+  return t;
+}
+
+template <int R, int KSPLIT>
+void launch_nvfp4_cfg(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
+  constexpr int rows_per_wg = R * (4 / KSPLIT);
+  const unsigned grid = (unsigned)((W.N + rows_per_wg - 1) / rows_per_wg);
+  k_gemv_nvfp4<R, KSPLIT><<<grid, 256, 0, stream>>>(W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
+}
+
+}  // namespace
+
+// Launch table: rows per wave R and the K split are picked per shape so that long rows
+// (down projection, K = 21504) still give every CU several waves.
+hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
+  if (W.N == 0) return hipSuccess;
+  if (W.K >= 16384)
+    launch_nvfp4_cfg<4, 4>(W, x, y, stream);
+  else if (W.K >= 8192 || W.N < 8192)
+    launch_nvfp4_cfg<2, 2>(W, x, y, stream);
+  else
+    launch_nvfp4_cfg<4, 1>(W, x, y, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  constexpr int R = 4;
+  const unsigned grid = (unsigned)((N + 4 * R - 1) / (4 * R));
+  k_gemv_bf16<R><<<grid, 256, 0, stream>>>(W, x, y, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace attnq

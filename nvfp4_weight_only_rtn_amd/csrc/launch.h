@@ -1,0 +1,19 @@
+// Host-side launchers implemented by the kernel translation units; called by attnq_api.hip
+// after argument validation. Each returns the hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/attnq.h"
+
+namespace attnq {
+
+hipError_t launch_reconstruct(const attnq_theta& theta, uint16_t* W_eff, hipStream_t stream);
+hipError_t launch_quantize(const attnq_theta& theta, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                           hipStream_t stream);
+hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream);
+hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream);
+hipError_t launch_gemm_nvfp4_small_m(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
+                                     hipStream_t stream);
+
+}  // namespace attnq

@@ -9,8 +9,9 @@ Recipe (the decode workloads the pages describe are Gemma 3 1B / Gemma 4 31B
 projections; weights and activations here are synthetic stand-ins of the same
 shapes):
 
-* every tensor is drawn from ``numpy.random.PCG64`` seeded by
-  ``SeedSequence([20261202, cfg, layer, proj, tensor])``;
+* every tensor is drawn, in row-major order, in blocks of 2^20 elements; block b comes from
+  ``numpy.random.PCG64`` seeded by ``SeedSequence([20261202, cfg, layer, proj, tensor, b])``
+  (blocks are filled in parallel; the values do not depend on the thread count);
 * values are drawn in float32, scaled, then rounded to bf16 by torch's
   float32 -> bfloat16 cast (round-to-nearest-even), and handed out as the raw
   uint16 bit patterns;
@@ -23,6 +24,9 @@ only ever timed, never compared with the oracle.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import torch
 
@@ -32,27 +36,53 @@ ROOT_SEED = 20261202
 T_W0, T_S, T_U, T_V, T_X = 0, 1, 2, 3, 4
 
 
-def _rng(cfg: int, layer: int, proj: int, tensor: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([ROOT_SEED, cfg, layer, proj, tensor])))
+GEN_BLOCK = 1 << 20
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
+
+
+def _rng(cfg: int, layer: int, proj: int, tensor: int, block: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([ROOT_SEED, cfg, layer, proj, tensor, block])))
+
+
+def _draw(shape, fill, key) -> np.ndarray:
+    """float32 array of `shape`; block b of the flat array is fill(generator_b, out_view)."""
+    out = np.empty(int(np.prod(shape)), dtype=np.float32)
+    nblk = (out.size + GEN_BLOCK - 1) // GEN_BLOCK
+
+    def one(b):
+        fill(_rng(*key, b), out[b * GEN_BLOCK:(b + 1) * GEN_BLOCK])
+    if nblk <= 1:
+        for b in range(nblk):
+            one(b)
+    else:
+        list(_pool().map(one, range(nblk)))
+    return out.reshape(shape)
 
 
 def _to_bf16_bits(a32: np.ndarray) -> np.ndarray:
     """float32 array -> uint16 bf16 bit patterns via torch's RNE cast (a library routine)."""
     t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32)).to(torch.bfloat16)
-    return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.view(torch.int16).numpy().view(np.uint16)
 
 
 def normal_bf16(shape, sigma: float, cfg: int, layer: int, proj: int, tensor: int) -> np.ndarray:
-    g = _rng(cfg, layer, proj, tensor)
-    a = g.standard_normal(size=shape, dtype=np.float32)
-    a *= np.float32(sigma)
-    return _to_bf16_bits(a)
+    def fill(g, o):
+        g.standard_normal(out=o, dtype=np.float32)
+        o *= np.float32(sigma)
+    return _to_bf16_bits(_draw(shape, fill, (cfg, layer, proj, tensor)))
 
 
 def uniform_bf16(shape, lo: float, hi: float, cfg: int, layer: int, proj: int, tensor: int) -> np.ndarray:
-    g = _rng(cfg, layer, proj, tensor)
-    a = g.uniform(lo, hi, size=shape).astype(np.float32)
-    return _to_bf16_bits(a)
+    def fill(g, o):
+        o[:] = g.uniform(lo, hi, size=o.size)
+    return _to_bf16_bits(_draw(shape, fill, (cfg, layer, proj, tensor)))
 
 
 def theta_bundle(N: int, K: int, r: int, cfg: int, layer: int, proj: int,

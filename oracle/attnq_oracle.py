@@ -145,11 +145,12 @@ def e2m1_encode_magnitude(aq: np.ndarray) -> np.ndarray:
 
     Grid 0, 0.5, 1, 1.5, 2, 3, 4, 6; the midpoints 0.25, 1.25, 2.5, 5 tie down
     to an even code, 0.75, 1.75, 3.5 tie up to an even code; above 5 saturates
-    to 6 (code 7).
+    to 6 (code 7). A NaN quotient can only come from 0/0 (a zero weight in a block whose step
+    d underflowed to zero) and encodes as 0.
     """
     a = np.asarray(aq, dtype=np.float32)
-    conds = [a <= 0.25, a < 0.75, a <= 1.25, a < 1.75, a <= 2.5, a < 3.5, a <= 5.0]
-    return np.select(conds, [0, 1, 2, 3, 4, 5, 6], default=7).astype(np.uint8)
+    conds = [np.isnan(a), a <= 0.25, a < 0.75, a <= 1.25, a < 1.75, a <= 2.5, a < 3.5, a <= 5.0]
+    return np.select(conds, [0, 0, 1, 2, 3, 4, 5, 6], default=7).astype(np.uint8)
 
 
 # ---------------------------------------------------------------------------
@@ -180,16 +181,22 @@ def reconstruct(W0: np.ndarray, s: np.ndarray | None = None, U: np.ndarray | Non
 # ---------------------------------------------------------------------------
 # NVFP4 RTN quantization ("NVFP4 quantization"; "What quantization actually saves")
 # ---------------------------------------------------------------------------
-def quantize_segment(W_eff: np.ndarray):
-    """One projection (segment): bf16 bits [n, K] -> (codes u8 [n, K/2], scales u8 [n, K/16], ts f32)."""
-    w = bf16_to_f32(W_eff)
-    n, K = w.shape
+def quantize_segment(W_eff: np.ndarray, rows=None):
+    """One projection (segment): bf16 bits [n, K] -> (codes u8 [n, K/2], scales u8 [n, K/16], ts f32).
+
+    rows: optional row indices; the amax is still taken over the whole segment, but codes and
+    scales are returned for those rows only (for sampled checks of large weights).
+    """
+    W_eff = np.asarray(W_eff)
+    n_all, K = W_eff.shape
     assert K % BLOCK == 0
-    codes = np.zeros((n, K // 2), dtype=np.uint8)
-    if n == 0:
-        return codes, np.zeros((0, K // BLOCK), dtype=np.uint8), np.float32(0.0)
+    if n_all == 0:
+        return np.zeros((0, K // 2), np.uint8), np.zeros((0, K // BLOCK), np.uint8), np.float32(0.0)
+    amax = np.float32(np.abs(bf16_to_f32(W_eff)).max())   # exact; NaN propagates
+    w = bf16_to_f32(W_eff if rows is None else W_eff[np.asarray(rows)])
+    n = w.shape[0]
     absw = np.abs(w)
-    amax = np.float32(absw.max())                          # exact; NaN propagates
+    codes = np.zeros((n, K // 2), dtype=np.uint8)
     if not np.isfinite(amax):
         scales = np.full((n, K // BLOCK), E4M3_NAN_CODE, dtype=np.uint8)
         return codes, scales, np.float32(np.nan)

@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI: the library loads, exports every call include/attnq.h
+declares, the ctypes descriptors match the C struct layout, and argument validation returns
+the documented status codes. No call here reaches a kernel launch: every argument set fails
+validation, which runs on the host before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnq.h")
+
+A = pytest.importorskip("nvfp4_weight_only_rtn_amd.attnq", reason="libattnq.so not built")
+
+# invalid-pointer calls are only made where no GPU can be reached by mistake
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="host-only validation test")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ATTNQ_API\s+[\w\s\*]+?\b(attnq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared_functions()
+    for n in ["attnq_reconstruct", "attnq_quantize_nvfp4", "attnq_gemv_nvfp4", "attnq_gemv_bf16",
+              "attnq_gemm_nvfp4_small_m", "attnq_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.raw_library()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(attnq_\w+)", out))
+    assert exported == set(_declared_functions())
+
+
+def test_status_strings():
+    for code, name in A.STATUS.items():
+        assert A.raw_library().attnq_status_string(code).decode().startswith(name)
+    assert b"unknown" in A.raw_library().attnq_status_string(99)
+
+
+def test_ctypes_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(f"""
+#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(attnq_theta), offsetof(attnq_theta, W0),
+         offsetof(attnq_theta, s), offsetof(attnq_theta, U), offsetof(attnq_theta, V),
+         offsetof(attnq_theta, N), offsetof(attnq_theta, K), offsetof(attnq_theta, r));
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(attnq_nvfp4), offsetof(attnq_nvfp4, codes),
+         offsetof(attnq_nvfp4, scales), offsetof(attnq_nvfp4, tensor_scale), offsetof(attnq_nvfp4, N),
+         offsetof(attnq_nvfp4, K), offsetof(attnq_nvfp4, n_seg), offsetof(attnq_nvfp4, seg_end),
+         offsetof(attnq_nvfp4, layout));
+  return 0;
+}}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(src), "-o", str(exe)], check=True)
+    c_theta, c_nv = [list(map(int, l.split())) for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split("\n")[:2]]
+    T, NV = A._Theta, A._NVFP4
+    assert c_theta == [ctypes.sizeof(T)] + [getattr(T, f).offset for f in ("W0", "s", "U", "V", "N", "K", "r")]
+    assert c_nv == [ctypes.sizeof(NV)] + [getattr(NV, f).offset for f in
+                                           ("codes", "scales", "tensor_scale", "N", "K", "n_seg", "seg_end", "layout")]
+
+
+# ---------------------------------------------------------------- validation (host only)
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
+
+
+def _nv(N=64, K=64, n_seg=1, seg_end=None, layout=0, codes=FAKE, scales=FAKE, ts=FAKE):
+    seg_end = [N] if seg_end is None else seg_end
+    return A._NVFP4(codes, scales, ts, N, K, n_seg, (ctypes.c_int32 * 4)(*(seg_end + [0] * (4 - len(seg_end)))), layout)
+
+
+def _th(N=64, K=64, r=0, W0=FAKE, s=None, U=None, V=None):
+    return A._Theta(W0, s, U, V, N, K, r)
+
+
+@no_gpu
+def test_reconstruct_validation():
+    lib = A.raw_library()
+    assert lib.attnq_reconstruct(None, FAKE, None) == 1
+    assert lib.attnq_reconstruct(ctypes.byref(_th(W0=None)), FAKE, None) == 1
+    assert lib.attnq_reconstruct(ctypes.byref(_th()), None, None) == 1
+    assert lib.attnq_reconstruct(ctypes.byref(_th(K=48)), FAKE, None) == 2       # K % 32 != 0
+    assert lib.attnq_reconstruct(ctypes.byref(_th(K=0)), FAKE, None) == 2
+    assert lib.attnq_reconstruct(ctypes.byref(_th(N=-1)), FAKE, None) == 2
+    assert lib.attnq_reconstruct(ctypes.byref(_th(r=65, U=FAKE, V=FAKE)), FAKE, None) == 2
+    assert lib.attnq_reconstruct(ctypes.byref(_th(r=4)), FAKE, None) == 1        # r > 0 needs U, V
+    assert lib.attnq_reconstruct(ctypes.byref(_th(W0=FAKE + 2)), FAKE, None) == 3
+    assert lib.attnq_reconstruct(ctypes.byref(_th()), FAKE + 8, None) == 3
+
+
+@no_gpu
+def test_quantize_validation():
+    lib = A.raw_library()
+    q = lib.attnq_quantize_nvfp4
+    assert q(ctypes.byref(_th()), None, 0, None) == 1
+    assert q(ctypes.byref(_th()), ctypes.byref(_nv(layout=1)), 0, None) == 5
+    assert q(ctypes.byref(_th(K=96)), ctypes.byref(_nv()), 0, None) == 2          # K mismatch
+    assert q(ctypes.byref(_th()), ctypes.byref(_nv()), 1, None) == 4              # seg out of range
+    assert q(ctypes.byref(_th(N=10)), ctypes.byref(_nv()), 0, None) == 4          # row count mismatch
+    nv = _nv(N=64, n_seg=3, seg_end=[32, 48, 64])
+    assert q(ctypes.byref(_th(N=32)), ctypes.byref(nv), 1, None) == 4             # seg 1 has 16 rows
+    assert q(ctypes.byref(_th()), ctypes.byref(_nv(n_seg=2, seg_end=[40, 30])), 0, None) == 4
+    assert q(ctypes.byref(_th()), ctypes.byref(_nv(n_seg=2, seg_end=[32, 60])), 0, None) == 4
+    assert q(ctypes.byref(_th()), ctypes.byref(_nv(n_seg=5)), 0, None) == 4
+    assert q(ctypes.byref(_th()), ctypes.byref(_nv(codes=FAKE + 4)), 0, None) == 3
+    assert q(ctypes.byref(_th()), ctypes.byref(_nv(scales=FAKE + 2)), 0, None) == 3
+
+
+@no_gpu
+def test_gemv_and_gemm_validation():
+    lib = A.raw_library()
+    nv = _nv()
+    assert lib.attnq_gemv_nvfp4(ctypes.byref(nv), None, FAKE, None) == 1
+    assert lib.attnq_gemv_nvfp4(ctypes.byref(nv), FAKE + 8, FAKE, None) == 3
+    assert lib.attnq_gemv_nvfp4(ctypes.byref(nv), FAKE, FAKE + 2, None) == 3
+    assert lib.attnq_gemv_nvfp4(ctypes.byref(_nv(K=16)), FAKE, FAKE, None) == 2
+    assert lib.attnq_gemv_bf16(FAKE, 10, 40, FAKE, FAKE, None) == 2
+    assert lib.attnq_gemv_bf16(FAKE, -1, 64, FAKE, FAKE, None) == 2
+    assert lib.attnq_gemv_bf16(None, 10, 64, FAKE, FAKE, None) == 1
+    assert lib.attnq_gemv_bf16(FAKE + 4, 10, 64, FAKE, FAKE, None) == 3
+    g = lib.attnq_gemm_nvfp4_small_m
+    assert g(ctypes.byref(nv), FAKE, 17, 64, FAKE, 64, None) == 2                 # M > 16
+    assert g(ctypes.byref(nv), FAKE, 4, 32, FAKE, 64, None) == 2                  # ldx < K
+    assert g(ctypes.byref(nv), FAKE, 4, 68, FAKE, 64, None) == 2                  # ldx % 8
+    assert g(ctypes.byref(nv), FAKE, 4, 64, FAKE, 32, None) == 2                  # ldy < N
+    assert g(ctypes.byref(nv), None, 4, 64, FAKE, 64, None) == 1
