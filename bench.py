@@ -129,28 +129,24 @@ def time_steps(fn, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
-def dominant_kernel_timing(model: Model, steps: int):
-    """Average duration of the gate|up NVFP4 GEMV launches (the largest byte share of a token),
-    measured with HIP events on the launch stream around each launch of eager steps."""
+def dominant_kernel_timing(model: Model, reps: int):
+    """Average duration of the fused gate|up NVFP4 GEMV (the largest byte share of a token):
+    HIP events on the launch stream bracket `reps` back-to-back passes over the 60 layers'
+    distinct gate|up weights (7.8 GB per pass, so every launch streams from HBM)."""
     A = model.A
-    pairs = []
+    launches = [lay["gate_up"] for lay in model.layers]
+    for (W, x, y, _, _) in launches:                      # warm-up pass
+        A.attnq_gemv_nvfp4(W, x, y)
     torch.cuda.synchronize()
-    for _ in range(steps):
-        for lay in model.layers:
-            for name in PROJ_NAMES:
-                W, x, y, _, _ = lay[name]
-                if name == "gate_up":
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    A.attnq_gemv_nvfp4(W, x, y)
-                    e1.record()
-                    pairs.append((e0, e1))
-                else:
-                    A.attnq_gemv_nvfp4(W, x, y)
-        A.attnq_gemv_bf16(model.lm_head, model.x_head, model.y_head)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for (W, x, y, _, _) in launches:
+            A.attnq_gemv_nvfp4(W, x, y)
+    e1.record()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in pairs]
-    return float(np.mean(ms)), float(np.median(ms)), len(ms)
+    n = reps * len(launches)
+    return e0.elapsed_time(e1) / n, n
 
 
 def load_path_timing(A, dev, model: Model, reps: int = 1):
@@ -229,8 +225,11 @@ def small_m_timing(A, model: Model, steps: int):
 
 
 def cpu_baseline():
-    """The oracle's dequantize + float64 GEMV on a bounded sample: the fused q|k|v and the o
-    projection of one 31B-like layer (55.1 M weights, 31.0 MB NVFP4)."""
+    """The oracle's dequantize + float64 GEMV on a bounded sample of the same workload: the four
+    projections of one 31B-like layer (q|k|v, o, gate|up, down: 401.8 M weights, 226 MB NVFP4).
+    The oracle's own quantization of the sample is setup (threads over segments), not timed."""
+    import concurrent.futures as cf
+
     import oracle as O
     from nvfp4_weight_only_rtn_amd import inputs
     try:
@@ -238,23 +237,32 @@ def cpu_baseline():
         blas = max([i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         blas = 1
+    specs = (("qkv", QKV_SEGS, HIDDEN), ("o", (O_SHAPE[0],), O_SHAPE[1]),
+             ("gate_up", GU_SEGS, HIDDEN), ("down", (DOWN_SHAPE[0],), DOWN_SHAPE[1]))
+    jobs = [(p, i, n, K) for p, (_, segs, K) in enumerate(specs) for i, n in enumerate(segs)]
+
+    def quantize(job):
+        p, i, n, K = job
+        W0 = inputs.theta_bundle(n, K, 0, cfg=2, layer=0, proj=10 * p + i, passthrough=True)[0]
+        return job, O.quantize_segment(W0)
+    with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        done = dict(ex.map(quantize, jobs))
     work = []
-    for name, segs, K in (("qkv", QKV_SEGS, HIDDEN), ("o", (O_SHAPE[0],), O_SHAPE[1])):
-        bundles = [inputs.theta_bundle(n, K, 0, cfg=2, layer=0, proj=p, passthrough=True) for p, n in enumerate(segs)]
-        parts = [O.quantize_segment(b[0]) for b in bundles]
-        codes = np.concatenate([p[0] for p in parts])
-        scales = np.concatenate([p[1] for p in parts])
-        ts = np.array([p[2] for p in parts], dtype=np.float32)
-        x = inputs.activation_bf16(1, K, 2, 0, 0)
+    for p, (_, segs, K) in enumerate(specs):
+        parts = [done[(p, i, n, K)] for i, n in enumerate(segs)]
+        codes = np.concatenate([q[0] for q in parts])
+        scales = np.concatenate([q[1] for q in parts])
+        ts = np.array([q[2] for q in parts], dtype=np.float32)
+        x = inputs.activation_bf16(1, K, 2, 0, p)
         work.append((codes, scales, ts, list(np.cumsum(segs)), x))
-    nbytes = sum(c.nbytes + s.nbytes + t.nbytes for c, s, t, _, _ in work)
+    nbytes = sum(c.nbytes + sc.nbytes + t.nbytes for c, sc, t, _, _ in work)
     t0 = time.perf_counter()
     for codes, scales, ts, ends, x in work:
         O.gemv_nvfp4(codes, scales, ts, x, ends)
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e12, 9), "unit": "TB/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"oracle dequantize + float64 GEMV of the fused q|k|v (6144x5376) and o (5376x4096) "
-                      f"projections of one 31B-like layer: {nbytes} NVFP4 bytes in {dt:.2f} s "
+            "sample": f"oracle dequantize + float64 GEMV over one 31B-like layer (q|k|v 6144x5376, o 5376x4096, "
+                      f"gate|up 43008x5376, down 5376x21504): {nbytes} NVFP4 bytes in {dt:.2f} s "
                       f"(numpy elementwise on 1 thread, BLAS on {blas}; affinity {len(os.sched_getaffinity(0))} cpus)"}
 
 
@@ -337,7 +345,7 @@ def main():
     tbps = bytes_step / (ms * 1e-3) / 1e12
     log(f"{'graph' if graph else 'eager'} {ms:.4f} ms/token, eager {eager_ms:.4f} ms/token, {tbps:.3f} TB/s")
 
-    dom_mean, dom_median, dom_n = dominant_kernel_timing(model, max(2, args.steps // 4))
+    dom_mean, dom_n = dominant_kernel_timing(model, max(3, args.steps // 2))
     W_gu = model.layers[0]["gate_up"][0]
     dom_bytes = nvfp4_bytes(W_gu.N, W_gu.K, 2)
     achieved = dom_bytes / (dom_mean * 1e-3) / 1e9
@@ -368,11 +376,11 @@ def main():
         "ms_per_token_eager": round(eager_ms, 5),
         "bytes_per_token": bytes_step,
         "weight_bytes_per_token": model.weight_bytes_per_step(),
-        "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4<4,1> (fused gate|up 43008x5376)",
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4_oneshot<2,1,3,true,8> (fused gate|up 43008x5376)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_mean * 1e3, 3),
-                     "median_launch_us": round(dom_median * 1e3, 3), "launches_timed": dom_n},
+                     "launches_timed": dom_n},
         "small_m": small_m,
         "load_path": load,
     }

@@ -116,6 +116,94 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
   }
 }
 
+// One-shot variant for rows of at most S*64 chunks per wave slice: every wave issues the code
+// and scale loads of its whole slice (S steps x R rows) before computing, which keeps the most
+// bytes in flight per wave. With XL the workgroup stages x in LDS once, transposed so that the
+// four 16-byte quarter reads of a chunk ([q][chunk]) are each bank-conflict free.
+template <int R, int KSPLIT, int S, bool XL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t* __restrict__ codes,
+                                                                   const uint8_t* __restrict__ scales,
+                                                                   const float* __restrict__ tensor_scale, SegTable segs,
+                                                                   const uint16_t* __restrict__ x, float* __restrict__ y,
+                                                                   int N, int K) {
+  static_assert(WAVES % KSPLIT == 0, "K split must divide the waves of a workgroup");
+  extern __shared__ u32x4 xs[];
+  constexpr int kRowGroups = WAVES / KSPLIT;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rg = wave / KSPLIT, ks = wave % KSPLIT;
+  const int row0 = (blockIdx.x * kRowGroups + rg) * R;
+  const int cpr = K >> 5;
+  const int slice = (cpr + KSPLIT - 1) / KSPLIT;
+  const int c_begin = ks * slice;
+  const int c_end = min(cpr, c_begin + slice);
+  const size_t code_pitch = (size_t)K >> 1;
+  const size_t scale_pitch = (size_t)K >> 4;
+
+  u32x4 cv[S][R];
+  uint32_t sv[S][R];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = min(c_begin + s * 64 + lane, cpr - 1);       // clamped: lanes past the slice reload a valid chunk
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(row0 + r, N - 1);
+      cv[s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + row * code_pitch) + c);
+      sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
+    }
+  }
+  if constexpr (XL) {
+    const u32x4* xg = reinterpret_cast<const u32x4*>(x);
+    for (int i = threadIdx.x; i < K / 8; i += 64 * WAVES) xs[(i & 3) * cpr + (i >> 2)] = xg[i];
+    __syncthreads();
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = c_begin + s * 64 + lane;
+    if (c < c_end) {
+      u32x4 x0, x1, x2, x3;
+      if constexpr (XL) {
+        x0 = xs[c]; x1 = xs[cpr + c]; x2 = xs[2 * cpr + c]; x3 = xs[3 * cpr + c];
+      } else {
+        const u32x4* xp = reinterpret_cast<const u32x4*>(x + (size_t)c * kChunkElems);
+        x0 = xp[0]; x1 = xp[1]; x2 = xp[2]; x3 = xp[3];
+      }
+      const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                               x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = chunk_dot(cv[s][r], sv[s][r], xw, acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  if constexpr (KSPLIT == 1) {
+    if (lane < R) {
+      float v = acc[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
+      const int row = row0 + lane;
+      if (row < N) y[row] = v * tensor_scale[segment_of(segs, row)];
+    }
+  } else {
+    __shared__ float part[WAVES][R];
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[wave][r] = acc[r];
+    }
+    __syncthreads();
+    if (ks == 0 && lane < R) {
+      float v = 0.0f;
+#pragma unroll
+      for (int k2 = 0; k2 < KSPLIT; ++k2) v += part[wave + k2][lane];
+      const int row = row0 + lane;
+      if (row < N) y[row] = v * tensor_scale[segment_of(segs, row)];
+    }
+  }
+}
+
 // bf16 weights: a lane owns one 16-byte chunk (8 bf16) of R rows per step; x chunk reused.
 template <int R>
 __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
@@ -164,24 +252,39 @@ SegTable seg_table(const attnq_nvfp4& W) {
 }
 
 template <int R, int KSPLIT>
-void launch_nvfp4_cfg(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
+void launch_nvfp4_loop(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
   constexpr int rows_per_wg = R * (4 / KSPLIT);
   const unsigned grid = (unsigned)((W.N + rows_per_wg - 1) / rows_per_wg);
   k_gemv_nvfp4<R, KSPLIT><<<grid, 256, 0, stream>>>(W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
 }
 
+template <int R, int KSPLIT, int S, bool XL, int WAVES>
+void launch_nvfp4_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
+  constexpr int rows_per_wg = R * (WAVES / KSPLIT);
+  const unsigned grid = (unsigned)((W.N + rows_per_wg - 1) / rows_per_wg);
+  const size_t lds = XL ? (size_t)W.K * 2 : 0;
+  k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES><<<grid, 64 * WAVES, lds, stream>>>(
+      W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
+}
+
 }  // namespace
 
-// Launch table: rows per wave R and the K split are picked per shape so that long rows
-// (down projection, K = 21504) still give every CU several waves.
+// Launch table (timed per shape on MI355X): rows of up to 6144 elements use the one-shot kernel
+// (x in LDS for short rows and for the tall fused gate|up, x from L1 for q|k|v); long rows (the
+// down projection, K = 21504) split K over the four waves of a workgroup in the loop kernel.
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
   if (W.N == 0) return hipSuccess;
+  const int cpr = W.K / 32;
   if (W.K >= 16384)
-    launch_nvfp4_cfg<4, 4>(W, x, y, stream);
-  else if (W.K >= 8192 || W.N < 8192)
-    launch_nvfp4_cfg<2, 2>(W, x, y, stream);
+    launch_nvfp4_loop<4, 4>(W, x, y, stream);
+  else if (cpr <= 128)
+    launch_nvfp4_oneshot<2, 2, 1, true, 8>(W, x, y, stream);        // K <= 4096: one step per slice
+  else if (cpr <= 192 && W.N >= 16384)
+    launch_nvfp4_oneshot<2, 1, 3, true, 8>(W, x, y, stream);        // fused gate|up 43008x5376
+  else if (cpr <= 192)
+    launch_nvfp4_oneshot<2, 1, 3, false, 4>(W, x, y, stream);       // fused q|k|v 6144x5376
   else
-    launch_nvfp4_cfg<4, 1>(W, x, y, stream);
+    launch_nvfp4_loop<2, 2>(W, x, y, stream);
   return hipGetLastError();
 }
 
