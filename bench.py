@@ -45,6 +45,18 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 VALU_FP32_PEAK_TFLOPS = 157.3  # published fp32 vector peak (packed), for the load path note
 PROJ_NAMES = ("qkv", "o", "gate_up", "down")
 
+# HBM traffic of one fused gate|up launch from the FETCH_SIZE / WRITE_SIZE passes recorded in
+# profiles/gemv_nvfp4_31b_token_traffic.md (FETCH scaled x1.9999, WRITE x1.0 by a 1 GiB copy).
+# Valid only for the kernel sources it was measured on: reported as null once they change.
+GATE_UP_TRAFFIC = {"sources_sha256_16": "d0a3c860b135b11a", "bytes": 130363169}
+
+
+def gemv_sources_hash() -> str:
+    import hashlib
+    csrc = os.path.join(ROOT, "nvfp4_weight_only_rtn_amd", "csrc")
+    data = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("gemv.hip", "attnq_device.h"))
+    return hashlib.sha256(data).hexdigest()[:16]
+
 
 def nvfp4_bytes(N: int, K: int, n_seg: int) -> int:
     """Algorithmic HBM bytes of one NVFP4 GEMV: codes + scales + tensor scales + x + y."""
@@ -378,7 +390,9 @@ def main():
         "weight_bytes_per_token": model.weight_bytes_per_step(),
         "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4_oneshot<2,1,3,true,8> (fused gate|up 43008x5376)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (GATE_UP_TRAFFIC["bytes"] if gemv_sources_hash() == GATE_UP_TRAFFIC["sources_sha256_16"]
+                                 else None),
                      "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_mean * 1e3, 3),
                      "launches_timed": dom_n},
         "small_m": small_m,
