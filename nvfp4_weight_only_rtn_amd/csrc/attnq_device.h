@@ -11,6 +11,7 @@ namespace attnq {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 16;          // elements per E4M3 block scale
 constexpr int kChunkElems = 32;     // one 16-byte code chunk = 32 fp4 = two blocks

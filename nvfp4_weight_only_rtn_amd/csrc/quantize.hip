@@ -6,10 +6,16 @@
 // landing page "Results" (round-to-nearest, no calibration); "Throughput", "What quantization
 // actually saves" (one float8_e4m3fn scale per 16 elements).
 //
-// One thread owns one 16-element block of a row: it rebuilds the block in registers, rounds
-// it to bf16 and then either folds |w| into the segment amax or emits 8 code bytes and one
-// scale byte. The fused path rebuilds twice (amax pass, then quantize pass) instead of
-// staging W_eff in HBM: at rank 0 that is 2 + 2 + 0.5625 B of traffic per element.
+// Rank 0 (passthrough or row scale only): one thread owns one 16-element block of a row, rebuilds
+// it in registers, rounds it to bf16 and then either folds |w| into the segment amax or emits 8
+// code bytes and one scale byte. The fused path rebuilds twice (amax pass, then quantize pass)
+// instead of staging W_eff in HBM: 2 + 2 + 0.5625 B of traffic per element.
+//
+// Rank r > 0: a workgroup rebuilds a 64-row x 256-column tile. V for the tile's columns and U for
+// its rows are staged in LDS as fp32 [k][column] and [k][row], 32 values of k at a time, and each
+// thread keeps a 4-row x 16-column block of fp32 accumulators, so every V value read from LDS
+// feeds four rows. The accumulation order (k ascending from +0, then s*W0 + acc) is the same in
+// both paths.
 #include "attnq_device.h"
 #include "launch.h"
 
@@ -25,13 +31,39 @@ struct Theta {
   int N, K, r;
 };
 
-// Rebuild 16 consecutive elements [col, col+16) of row `row` as bf16 bit patterns.
-__device__ __forceinline__ void rebuild_block(const Theta& t, int row, int col, uint32_t wb[kBlock]) {
+// Round a rebuilt 16-element block (bf16 bit patterns) to NVFP4 with the segment's amax bits:
+// 8 packed code bytes (even element in the low nibble) and one E4M3 scale code.
+__device__ __forceinline__ void quantize_block(const uint32_t wb[kBlock], uint32_t amax_bits, uint32_t packed[2],
+                                               uint32_t& scale_code) {
+  const float ts = tensor_scale_from_amax_bits(amax_bits);
+  const float six_ts = 6.0f * ts;
+  uint32_t bmax = 0;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) bmax = max(bmax, wb[i] & 0x7FFFu);
+  const float bamax = bf16_bits_to_f32(bmax);
+  const float sb = (amax_bits == 0u) ? 0.0f : bamax / six_ts;
+  const uint32_t S = e4m3_encode_nonneg(sb);
+  const float d = e4m3_to_f32(S) * ts;
+  packed[0] = 0u;
+  packed[1] = 0u;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) {
+    const float w = bf16_bits_to_f32(wb[i]);
+    const uint32_t mag = (S == 0u) ? 0u : e2m1_magnitude(__builtin_fabsf(w / d));
+    const uint32_t code = ((wb[i] >> 12) & 8u) | mag;
+    packed[i >> 3] |= code << (4 * (i & 7));
+  }
+  scale_code = S;
+}
+
+// ---------------------------------------------------------------------------------- rank 0
+// Rebuild 16 consecutive elements [col, col+16) of row `row` as bf16 bit patterns (r == 0).
+__device__ __forceinline__ void rebuild_block_r0(const Theta& t, int row, int col, uint32_t wb[kBlock]) {
   const u32x4* src = reinterpret_cast<const u32x4*>(t.W0 + (size_t)row * t.K + col);
-  u32x4 a = __builtin_nontemporal_load(src);
-  u32x4 b = __builtin_nontemporal_load(src + 1);
-  uint32_t w0[kBlock / 2] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  if (t.s == nullptr && t.r == 0) {                 // passthrough: W_eff = W0 bit for bit
+  const u32x4 a = __builtin_nontemporal_load(src);
+  const u32x4 b = __builtin_nontemporal_load(src + 1);
+  const uint32_t w0[kBlock / 2] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  if (t.s == nullptr) {                             // passthrough: W_eff = W0 bit for bit
 #pragma unroll
     for (int i = 0; i < kBlock / 2; ++i) {
       wb[2 * i] = w0[i] & 0xFFFFu;
@@ -39,39 +71,21 @@ __device__ __forceinline__ void rebuild_block(const Theta& t, int row, int col, 
     }
     return;
   }
-  const float si = t.s ? bf16_bits_to_f32(t.s[row]) : 1.0f;
-  float w[kBlock];
+  const float si = bf16_bits_to_f32(t.s[row]);
 #pragma unroll
-  for (int i = 0; i < kBlock / 2; ++i) {
-    w[2 * i] = bf16_bits_to_f32(w0[i] & 0xFFFFu);
-    w[2 * i + 1] = bf16_bits_to_f32(w0[i] >> 16);
+  for (int i = 0; i < kBlock / 2; ++i) {             // bf16 x bf16 products are exact in fp32
+    wb[2 * i] = f32_to_bf16_bits(si * bf16_bits_to_f32(w0[i] & 0xFFFFu));
+    wb[2 * i + 1] = f32_to_bf16_bits(si * bf16_bits_to_f32(w0[i] >> 16));
   }
-  if (t.r == 0) {
-#pragma unroll
-    for (int i = 0; i < kBlock; ++i) wb[i] = f32_to_bf16_bits(si * w[i]);   // product is exact
-    return;
-  }
-  float acc[kBlock];
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) acc[i] = 0.0f;
-  const uint16_t* urow = t.U + (size_t)row * t.r;
-  const uint16_t* vblk = t.V + (size_t)col * t.r;
-  for (int k = 0; k < t.r; ++k) {                   // k ascending: one fp32 rounding per step
-    const float u = bf16_bits_to_f32(urow[k]);
-#pragma unroll
-    for (int i = 0; i < kBlock; ++i) acc[i] = __builtin_fmaf(u, bf16_bits_to_f32(vblk[i * t.r + k]), acc[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) wb[i] = f32_to_bf16_bits(__builtin_fmaf(si, w[i], acc[i]));
 }
 
-__global__ __launch_bounds__(256) void k_reconstruct(Theta t, uint16_t* __restrict__ out, int64_t nblocks) {
+__global__ __launch_bounds__(256) void k_reconstruct_r0(Theta t, uint16_t* __restrict__ out, int64_t nblocks) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   const int bpr = t.K / kBlock;
   const int row = (int)(b / bpr), col = (int)(b % bpr) * kBlock;
   uint32_t wb[kBlock];
-  rebuild_block(t, row, col, wb);
+  rebuild_block_r0(t, row, col, wb);
   u32x4 lo = {wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16), wb[4] | (wb[5] << 16), wb[6] | (wb[7] << 16)};
   u32x4 hi = {wb[8] | (wb[9] << 16), wb[10] | (wb[11] << 16), wb[12] | (wb[13] << 16), wb[14] | (wb[15] << 16)};
   u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)row * t.K + col);
@@ -83,19 +97,10 @@ __global__ void k_zero_slot(uint32_t* slot) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *slot = 0u;
 }
 
-// amax over the segment as the max of |w| bit patterns (order-free, hence deterministic).
-// NaN patterns sort above +inf, so a NaN anywhere leaves a non-finite amax.
-__global__ __launch_bounds__(256) void k_amax(Theta t, uint32_t* slot, int64_t nblocks) {
+// Workgroup max of per-thread |w| bit patterns, folded into the segment slot with atomicMax.
+// The max of bit patterns is order-free, hence deterministic; NaN patterns sort above +inf.
+__device__ __forceinline__ void fold_amax(uint32_t m, uint32_t* slot) {
   __shared__ uint32_t red[4];
-  uint32_t m = 0;
-  const int bpr = t.K / kBlock;
-  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * 256) {
-    const int row = (int)(b / bpr), col = (int)(b % bpr) * kBlock;
-    uint32_t wb[kBlock];
-    rebuild_block(t, row, col, wb);
-#pragma unroll
-    for (int i = 0; i < kBlock; ++i) m = max(m, (wb[i] & 0x7FFFu) << 16);
-  }
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -105,8 +110,21 @@ __global__ __launch_bounds__(256) void k_amax(Theta t, uint32_t* slot, int64_t n
   }
 }
 
-__global__ __launch_bounds__(256) void k_quantize(Theta t, const uint32_t* __restrict__ slot, uint8_t* __restrict__ codes,
-                                                  uint8_t* __restrict__ scales, int64_t nblocks) {
+__global__ __launch_bounds__(256) void k_amax_r0(Theta t, uint32_t* slot, int64_t nblocks) {
+  uint32_t m = 0;
+  const int bpr = t.K / kBlock;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * 256) {
+    const int row = (int)(b / bpr), col = (int)(b % bpr) * kBlock;
+    uint32_t wb[kBlock];
+    rebuild_block_r0(t, row, col, wb);
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) m = max(m, (wb[i] & 0x7FFFu) << 16);
+  }
+  fold_amax(m, slot);
+}
+
+__global__ __launch_bounds__(256) void k_quantize_r0(Theta t, const uint32_t* __restrict__ slot, uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales, int64_t nblocks) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   const int bpr = t.K / kBlock;
@@ -120,26 +138,166 @@ __global__ __launch_bounds__(256) void k_quantize(Theta t, const uint32_t* __res
     return;
   }
   uint32_t wb[kBlock];
-  rebuild_block(t, row, cb * kBlock, wb);
-  const float ts = tensor_scale_from_amax_bits(amax_bits);
-  const float six_ts = 6.0f * ts;
-  uint32_t bmax = 0;
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) bmax = max(bmax, wb[i] & 0x7FFFu);
-  const float bamax = bf16_bits_to_f32(bmax);
-  const float sb = (amax_bits == 0u) ? 0.0f : bamax / six_ts;
-  const uint32_t S = e4m3_encode_nonneg(sb);
-  const float d = e4m3_to_f32(S) * ts;
-  uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) {
-    const float w = bf16_bits_to_f32(wb[i]);
-    const uint32_t mag = (S == 0u) ? 0u : e2m1_magnitude(__builtin_fabsf(w / d));
-    const uint32_t code = ((wb[i] >> 12) & 8u) | mag;
-    packed[i >> 3] |= code << (4 * (i & 7));
-  }
+  rebuild_block_r0(t, row, cb * kBlock, wb);
+  uint32_t packed[2], S;
+  quantize_block(wb, amax_bits, packed, S);
   *cdst = u32x2{packed[0], packed[1]};
   *sdst = (uint8_t)S;
+}
+
+// ---------------------------------------------------------------------------------- rank > 0
+constexpr int kTileRows = 64;
+constexpr int kTileCols = 256;
+constexpr int kRowsPerThread = 4;   // 256 threads = 16 column blocks x 16 row groups of 4 rows
+constexpr int kRankChunk = 32;      // values of k staged in LDS at a time
+// LDS row strides (floats) of the staged V [k][column] and U [k][row] tiles: padded by 4 so the
+// transposing writes spread over the banks while rows stay 16-byte aligned for the f32x4 reads.
+constexpr int kVStride = kTileCols + 4;
+constexpr int kUStride = kTileRows + 4;
+
+enum LowRankPass { kPassAmax = 0, kPassQuantize = 1, kPassReconstruct = 2 };
+
+size_t lowrank_lds_bytes(int r) { return (size_t)min(r, kRankChunk) * (kVStride + kUStride) * 4; }
+
+// e / n for 0 <= e < 2^16 and 1 <= n <= 32: the reciprocal product lands at least 1/64 away from
+// the next integer, far beyond its rounding error.
+__device__ __forceinline__ int div_small(int e, float inv_n) { return (int)(((float)e + 0.5f) * inv_n); }
+
+// Copy rows base .. base+nrow-1 (clamped to `limit`, zero past it) of a row-major [*, r] bf16 matrix,
+// columns k0 .. k0+kn-1, into LDS as fp32 dst[k * stride + row]. Consecutive threads read
+// consecutive elements; each thread issues its (up to) 8 loads before any LDS write.
+template <int NROW>
+__device__ __forceinline__ void stage_transposed(const uint16_t* __restrict__ src, int r, int base, int limit, int k0,
+                                                 int kn, float inv_kn, float* dst, int stride) {
+  const int total = NROW * kn;
+  for (int e0 = 0; e0 < total; e0 += 8 * 256) {
+    uint16_t v[8];
+    int at[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {                 // clamped, branch-free loads, all issued first
+      const int e = min(e0 + j * 256 + (int)threadIdx.x, total - 1);
+      const int row = div_small(e, inv_kn), k = e - row * kn;
+      v[j] = src[(size_t)min(base + row, limit - 1) * r + k0 + k];
+      at[j] = (base + row < limit) ? k * stride + row : ~(k * stride + row);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (e0 + j * 256 + (int)threadIdx.x < total) {
+        if (at[j] >= 0) dst[at[j]] = bf16_bits_to_f32(v[j]);
+        else dst[~at[j]] = 0.0f;
+      }
+    }
+  }
+}
+
+// One thread rebuilds rows row0 + 4*rg .. +3, columns col .. col+15 of a 64 x 256 tile.
+template <int PASS>
+__global__ __launch_bounds__(256) void k_lowrank_tile(Theta t, uint32_t* slot, uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales, uint16_t* __restrict__ out,
+                                                      int tiles_c) {
+  extern __shared__ float lds[];
+  const int r = t.r;
+  const int rc = min(r, kRankChunk);
+  float* vt = lds;                              // [rc][kVStride]
+  float* ut = lds + (size_t)rc * kVStride;      // [rc][kUStride]
+  const int tile_r = blockIdx.x / tiles_c, tile_c = blockIdx.x % tiles_c;
+  const int row0 = tile_r * kTileRows, col0 = tile_c * kTileCols;
+
+  uint32_t amax_bits = 0;
+  if (PASS == kPassQuantize) {
+    amax_bits = *slot;
+    if (amax_bits >= 0x7F800000u) {               // non-finite segment: NaN scales, zero codes
+      const int cb = threadIdx.x & 15, rg = threadIdx.x >> 4;
+      const int col = col0 + cb * kBlock;
+      for (int rr = 0; rr < kRowsPerThread; ++rr) {
+        const int row = row0 + rg * kRowsPerThread + rr;
+        if (row < t.N && col < t.K) {
+          *reinterpret_cast<u32x2*>(codes + (size_t)row * (t.K / 2) + col / 2) = u32x2{0u, 0u};
+          scales[(size_t)row * (t.K / kBlock) + col / kBlock] = 0x7F;
+        }
+      }
+      return;
+    }
+  }
+
+  const int cb = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int col = col0 + cb * kBlock;
+  const bool col_ok = col < t.K;                 // K % 16 == 0, so the whole block is inside
+  float acc[kRowsPerThread][kBlock];
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerThread; ++rr)
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) acc[rr][i] = 0.0f;
+  for (int k0 = 0; k0 < r; k0 += kRankChunk) {
+    const int kn = min(kRankChunk, r - k0);
+    if (k0 > 0) __syncthreads();                 // previous chunk fully consumed
+    // stage V (tile columns) and U (tile rows) for k0 .. k0+kn-1, transposed to [k][.]; zero
+    // outside the matrix
+    const float inv_kn = 1.0f / (float)kn;
+    stage_transposed<kTileCols>(t.V, r, col0, t.K, k0, kn, inv_kn, vt, kVStride);
+    stage_transposed<kTileRows>(t.U, r, row0, t.N, k0, kn, inv_kn, ut, kUStride);
+    __syncthreads();
+    for (int k = 0; k < kn; ++k) {               // k ascending: one fp32 rounding per step
+      const f32x4* vp = reinterpret_cast<const f32x4*>(vt + k * kVStride + cb * kBlock);
+      const f32x4 v0 = vp[0], v1 = vp[1], v2 = vp[2], v3 = vp[3];
+      const float v[kBlock] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                               v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+      const f32x4 up = *reinterpret_cast<const f32x4*>(ut + k * kUStride + rg * kRowsPerThread);
+      const float u[kRowsPerThread] = {up.x, up.y, up.z, up.w};
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerThread; ++rr)
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) acc[rr][i] = __builtin_fmaf(u[rr], v[i], acc[rr][i]);
+    }
+  }
+
+  int rows[kRowsPerThread];
+  u32x4 w0a[kRowsPerThread], w0b[kRowsPerThread];
+  float si[kRowsPerThread];
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerThread; ++rr) {
+    rows[rr] = row0 + rg * kRowsPerThread + rr;
+    const int row = min(rows[rr], t.N - 1);      // clamped load; results of rows past N are dropped
+    const int cc = col_ok ? col : 0;
+    const u32x4* src = reinterpret_cast<const u32x4*>(t.W0 + (size_t)row * t.K + cc);
+    w0a[rr] = __builtin_nontemporal_load(src);
+    w0b[rr] = __builtin_nontemporal_load(src + 1);
+    si[rr] = t.s ? bf16_bits_to_f32(t.s[row]) : 1.0f;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerThread; ++rr) {
+    const uint32_t ww[8] = {w0a[rr].x, w0a[rr].y, w0a[rr].z, w0a[rr].w, w0b[rr].x, w0b[rr].y, w0b[rr].z, w0b[rr].w};
+    uint32_t wb[kBlock];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wb[2 * i] = f32_to_bf16_bits(__builtin_fmaf(si[rr], bf16_bits_to_f32(ww[i] & 0xFFFFu), acc[rr][2 * i]));
+      wb[2 * i + 1] = f32_to_bf16_bits(__builtin_fmaf(si[rr], bf16_bits_to_f32(ww[i] >> 16), acc[rr][2 * i + 1]));
+    }
+    const bool ok = col_ok && rows[rr] < t.N;
+    if (PASS == kPassAmax) {
+      if (ok) {
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) m = max(m, (wb[i] & 0x7FFFu) << 16);
+      }
+    } else if (PASS == kPassQuantize) {
+      if (ok) {
+        uint32_t packed[2], S;
+        quantize_block(wb, amax_bits, packed, S);
+        *reinterpret_cast<u32x2*>(codes + (size_t)rows[rr] * (t.K / 2) + col / 2) = u32x2{packed[0], packed[1]};
+        scales[(size_t)rows[rr] * (t.K / kBlock) + col / kBlock] = (uint8_t)S;
+      }
+    } else {
+      if (ok) {
+        u32x4 lo = {wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16), wb[4] | (wb[5] << 16), wb[6] | (wb[7] << 16)};
+        u32x4 hi = {wb[8] | (wb[9] << 16), wb[10] | (wb[11] << 16), wb[12] | (wb[13] << 16), wb[14] | (wb[15] << 16)};
+        u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)rows[rr] * t.K + col);
+        dst[0] = lo;
+        dst[1] = hi;
+      }
+    }
+  }
+  if (PASS == kPassAmax) fold_amax(m, slot);
 }
 
 __global__ void k_finalize(uint32_t* slot) {
@@ -151,27 +309,43 @@ __global__ void k_finalize(uint32_t* slot) {
 
 Theta to_theta(const attnq_theta& t) { return Theta{t.W0, t.s, t.U, t.V, t.N, t.K, t.r}; }
 
+template <int PASS>
+void launch_lowrank(const Theta& t, uint32_t* slot, uint8_t* codes, uint8_t* scales, uint16_t* out, hipStream_t stream) {
+  const int tiles_r = (t.N + kTileRows - 1) / kTileRows;
+  const int tiles_c = (t.K + kTileCols - 1) / kTileCols;
+  k_lowrank_tile<PASS><<<(unsigned)tiles_r * tiles_c, 256, lowrank_lds_bytes(t.r), stream>>>(t, slot, codes, scales, out,
+                                                                                           tiles_c);
+}
+
 }  // namespace
 
 hipError_t launch_reconstruct(const attnq_theta& th, uint16_t* out, hipStream_t stream) {
+  const Theta t = to_theta(th);
   const int64_t nblocks = (int64_t)th.N * (th.K / kBlock);
   if (nblocks == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((nblocks + 255) / 256);
-  k_reconstruct<<<grid, 256, 0, stream>>>(to_theta(th), out, nblocks);
+  if (t.r == 0)
+    k_reconstruct_r0<<<(unsigned)((nblocks + 255) / 256), 256, 0, stream>>>(t, out, nblocks);
+  else
+    launch_lowrank<kPassReconstruct>(t, nullptr, nullptr, nullptr, out, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(const attnq_theta& th, uint8_t* codes, uint8_t* scales, float* tensor_scale,
                            hipStream_t stream) {
-  Theta t = to_theta(th);
+  const Theta t = to_theta(th);
   const int64_t nblocks = (int64_t)th.N * (th.K / kBlock);
   uint32_t* slot = reinterpret_cast<uint32_t*>(tensor_scale);
   k_zero_slot<<<1, 64, 0, stream>>>(slot);
   if (nblocks > 0) {
-    const int64_t want = (nblocks + 255) / 256;
-    const unsigned amax_grid = (unsigned)(want < 4096 ? want : 4096);
-    k_amax<<<amax_grid, 256, 0, stream>>>(t, slot, nblocks);
-    k_quantize<<<(unsigned)want, 256, 0, stream>>>(t, slot, codes, scales, nblocks);
+    if (t.r == 0) {
+      const int64_t want = (nblocks + 255) / 256;
+      const unsigned amax_grid = (unsigned)(want < 4096 ? want : 4096);
+      k_amax_r0<<<amax_grid, 256, 0, stream>>>(t, slot, nblocks);
+      k_quantize_r0<<<(unsigned)want, 256, 0, stream>>>(t, slot, codes, scales, nblocks);
+    } else {
+      launch_lowrank<kPassAmax>(t, slot, nullptr, nullptr, nullptr, stream);
+      launch_lowrank<kPassQuantize>(t, slot, codes, scales, nullptr, stream);
+    }
   }
   k_finalize<<<1, 64, 0, stream>>>(slot);
   return hipGetLastError();

@@ -47,7 +47,7 @@ def test_quantize_small_decoder_layer(A):
     _check_quant(A, [inputs.theta_bundle(1152, 6912, 4, cfg=1, layer=L, proj=6)], 6912, "1B-like down")
 
 
-@pytest.mark.parametrize("r,uv", [(1, 1e-2), (16, 1e-3), (16, 1e-2), (64, 1e-2)])
+@pytest.mark.parametrize("r,uv", [(1, 1e-2), (16, 1e-3), (16, 1e-2), (33, 1e-2), (64, 1e-2)])
 def test_quantize_ranks(A, r, uv):
     b = inputs.theta_bundle(200, 320, r, cfg=9, layer=20, proj=r, uv_sigma=uv)
     _check_quant(A, [b], 320, f"rank {r} uv {uv} 200x320")
@@ -137,7 +137,7 @@ def test_quantize_empty_is_noop(A):
     assert host(W.tensor_scale)[0] == 0.0
 
 
-@pytest.mark.parametrize("case", ["passthrough", "scale_only", "rank4", "rank16_stress", "rank64"])
+@pytest.mark.parametrize("case", ["passthrough", "scale_only", "rank4", "rank16_stress", "rank40", "rank64"])
 def test_reconstruct_bit_exact(A, case):
     N, K = 300, 448
     if case == "passthrough":
@@ -148,6 +148,8 @@ def test_reconstruct_bit_exact(A, case):
         b = inputs.theta_bundle(N, K, 4, cfg=9, layer=24, proj=2)
     elif case == "rank16_stress":
         b = inputs.theta_bundle(N, K, 16, cfg=9, layer=24, proj=3, uv_sigma=1e-2)
+    elif case == "rank40":                      # two staged chunks of k, the second partial
+        b = inputs.theta_bundle(N, K, 40, cfg=9, layer=24, proj=5, uv_sigma=1e-2)
     else:
         b = inputs.theta_bundle(N, K, 64, cfg=9, layer=24, proj=4, uv_sigma=1e-2)
     say(f"reconstruct {case} {N}x{K}")
