@@ -131,3 +131,44 @@ def test_small_m(A, M):
     Y_ref = O.gemm_nvfp4_small_m(c, s, t, X, seg_end)
     absdot = O.abs_dot(c, s, t, X, seg_end)
     assert_close_products(Y[:M, :W.N], Y_ref, absdot, f"small-M {M}")
+
+
+# ragged K (K % 128 in {32, 64, 96} exercises the 32-element tail), ragged 16-row tiles, both
+# launch configurations (N >= 16384 uses two row tiles per wave), and every token-row count class
+@pytest.mark.parametrize("N,K,M", [(1, 32, 1), (17, 96, 3), (333, 1184, 16), (1000, 1248, 5), (4097, 2080, 8),
+                                   (16385, 224, 4), (16400, 1152 + 64, 13), (600, 21504 + 32, 2)])
+def test_small_m_ragged(A, N, K, M):
+    b = inputs.theta_bundle(N, K, 0, cfg=9, layer=31, proj=N % 97, passthrough=True)
+    say(f"small-M ragged {M}x{N}x{K}")
+    W, seg_end = gpu_quantize(A, [b], K)
+    c, s, t, _ = oracle_quantize([b])
+    X = inputs.activation_bf16(M, K, 9, 31, N % 89)
+    Y = torch.full((M, N), np.nan, dtype=torch.float32, device="cuda")
+    A.attnq_gemm_nvfp4_small_m(W, dev(X), Y)
+    torch.cuda.synchronize()
+    assert_close_products(host(Y), O.gemm_nvfp4_small_m(c, s, t, X, seg_end), O.abs_dot(c, s, t, X, seg_end),
+                          f"small-M ragged {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M_small,M_big", [(1, 4), (2, 3), (5, 16), (8, 13)])
+def test_small_m_rows_are_independent_of_padding(A, M_small, M_big):
+    """Token rows m < M must not depend on how many rows follow or what they hold: within one
+    launch class (M <= 4, and 4 < M <= 16, which share a kernel and its summation order), the
+    first M_small rows of the M_big product equal the M_small product bit for bit, also after
+    the rows past M_small are overwritten."""
+    N, K = 2048, 1152
+    b = inputs.theta_bundle(N, K, 0, cfg=9, layer=32, proj=0, passthrough=True)
+    W, _ = gpu_quantize(A, [b], K)
+    X = dev(inputs.activation_bf16(16, K, 9, 32, 1))
+    Xb = X.clone()
+    Xb[M_small:] = dev(inputs.activation_bf16(16, K, 9, 32, 2))[M_small:]
+    Yb = torch.empty((M_big, N), dtype=torch.float32, device="cuda")
+    Yb2 = torch.empty((M_big, N), dtype=torch.float32, device="cuda")
+    Ys = torch.empty((M_small, N), dtype=torch.float32, device="cuda")
+    A.attnq_gemm_nvfp4_small_m(W, X[:M_big], Yb)
+    A.attnq_gemm_nvfp4_small_m(W, Xb[:M_big], Yb2)
+    A.attnq_gemm_nvfp4_small_m(W, X[:M_small], Ys)
+    torch.cuda.synchronize()
+    s_bits = host(Ys).view(np.uint32)
+    assert np.array_equal(s_bits, host(Yb)[:M_small].view(np.uint32))
+    assert np.array_equal(s_bits, host(Yb2)[:M_small].view(np.uint32))
