@@ -119,14 +119,17 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 // One-shot variant for rows of at most S*64 chunks per wave slice: every wave issues the code
 // and scale loads of its whole slice (S steps x R rows) before computing, which keeps the most
 // bytes in flight per wave. With XL the workgroup stages x in LDS once, transposed so that the
-// four 16-byte quarter reads of a chunk ([q][chunk]) are each bank-conflict free.
-template <int R, int KSPLIT, int S, bool XL, int WAVES>
+// four 16-byte quarter reads of a chunk ([q][chunk]) are each bank-conflict free. XFIRST issues
+// the x loads (at most XI 16-byte pieces per thread) before the weight loads, so the LDS staging
+// waits for x only; otherwise x is loaded after the weights (better for the tall gate|up shape).
+template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t* __restrict__ codes,
                                                                    const uint8_t* __restrict__ scales,
                                                                    const float* __restrict__ tensor_scale, SegTable segs,
                                                                    const uint16_t* __restrict__ x, float* __restrict__ y,
                                                                    int N, int K) {
   static_assert(WAVES % KSPLIT == 0, "K split must divide the waves of a workgroup");
+  static_assert(!XFIRST || XL, "x-first staging is an LDS staging");
   extern __shared__ u32x4 xs[];
   constexpr int kRowGroups = WAVES / KSPLIT;
   const int lane = threadIdx.x & 63;
@@ -139,7 +142,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   const int c_end = min(cpr, c_begin + slice);
   const size_t code_pitch = (size_t)K >> 1;
   const size_t scale_pitch = (size_t)K >> 4;
+  const u32x4* xg = reinterpret_cast<const u32x4*>(x);
 
+  u32x4 xst[XI];
+  if constexpr (XFIRST) {
+#pragma unroll
+    for (int j = 0; j < XI; ++j) xst[j] = xg[min((int)threadIdx.x + j * 64 * WAVES, K / 8 - 1)];
+  }
   u32x4 cv[S][R];
   uint32_t sv[S][R];
 #pragma unroll
@@ -152,8 +161,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
       sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
     }
   }
-  if constexpr (XL) {
-    const u32x4* xg = reinterpret_cast<const u32x4*>(x);
+  if constexpr (XFIRST) {
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+      const int i = threadIdx.x + j * 64 * WAVES;
+      if (i < K / 8) xs[(i & 3) * cpr + (i >> 2)] = xst[j];
+    }
+    __syncthreads();
+  } else if constexpr (XL) {
     for (int i = threadIdx.x; i < K / 8; i += 64 * WAVES) xs[(i & 3) * cpr + (i >> 2)] = xg[i];
     __syncthreads();
   }
@@ -258,31 +273,33 @@ void launch_nvfp4_loop(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStr
   k_gemv_nvfp4<R, KSPLIT><<<grid, 256, 0, stream>>>(W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
 }
 
-template <int R, int KSPLIT, int S, bool XL, int WAVES>
+template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1>
 void launch_nvfp4_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
   constexpr int rows_per_wg = R * (WAVES / KSPLIT);
   const unsigned grid = (unsigned)((W.N + rows_per_wg - 1) / rows_per_wg);
   const size_t lds = XL ? (size_t)W.K * 2 : 0;
-  k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES><<<grid, 64 * WAVES, lds, stream>>>(
+  k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI><<<grid, 64 * WAVES, lds, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
 }
 
 }  // namespace
 
-// Launch table (timed per shape on MI355X): rows of up to 6144 elements use the one-shot kernel
-// (x in LDS for short rows and for the tall fused gate|up, x from L1 for q|k|v); long rows (the
-// down projection, K = 21504) split K over the four waves of a workgroup in the loop kernel.
+// Launch table (timed per shape on MI355X, 31B-like shapes streamed cold): rows of up to 6144
+// elements use the one-shot kernel. The fused gate|up (43008 x 5376) stages x in LDS after its
+// weight loads; q|k|v (6144 x 5376, one row per wave) and o (5376 x 4096, two rows per wave,
+// two steps) stage x first. Long rows (the down projection, K = 21504) split K over the four
+// waves of a workgroup in the loop kernel.
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
   if (W.N == 0) return hipSuccess;
   const int cpr = W.K / 32;
   if (W.K >= 16384)
     launch_nvfp4_loop<4, 4>(W, x, y, stream);
   else if (cpr <= 128)
-    launch_nvfp4_oneshot<2, 2, 1, true, 8>(W, x, y, stream);        // K <= 4096: one step per slice
+    launch_nvfp4_oneshot<2, 1, 2, true, 4, true, 2>(W, x, y, stream);    // K <= 4096: two steps per row (x: 2 x 256 >= K/8)
   else if (cpr <= 192 && W.N >= 16384)
-    launch_nvfp4_oneshot<2, 1, 3, true, 8>(W, x, y, stream);        // fused gate|up 43008x5376
+    launch_nvfp4_oneshot<2, 1, 3, true, 8>(W, x, y, stream);             // fused gate|up 43008x5376
   else if (cpr <= 192)
-    launch_nvfp4_oneshot<2, 1, 3, false, 4>(W, x, y, stream);       // fused q|k|v 6144x5376
+    launch_nvfp4_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 2 x 512 >= K/8)
   else
     launch_nvfp4_loop<2, 2>(W, x, y, stream);
   return hipGetLastError();
