@@ -31,52 +31,109 @@ struct Theta {
   int N, K, r;
 };
 
-// Round a rebuilt 16-element block (bf16 bit patterns) to NVFP4 with the segment's amax bits:
-// 8 packed code bytes (even element in the low nibble) and one E4M3 scale code.
-__device__ __forceinline__ void quantize_block(const uint32_t wb[kBlock], uint32_t amax_bits, uint32_t packed[2],
+// Two fp32 values -> two bf16 (round to nearest even, NaN kept quiet), packed low = first. The
+// gfx950 converter (v_cvt_pk_bf16_f32) matches the bit-level rule of f32_to_bf16_bits exactly.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+
+// Two fp32 quotients -> two E2M1 codes in byte `j` of `acc` (even element in the low nibble):
+// v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to the nearest grid value with ties to the even
+// code, saturates at 6 and copies the sign, which is e2m1_magnitude plus the sign bit for every
+// non-NaN input.
+__device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t acc, float a, float b, int j) {
+  switch (j) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, 3);
+  }
+}
+
+// Round a rebuilt 16-element block (eight packed bf16 pairs, element 2i in the low half of
+// wp[i]) to NVFP4 with the segment's amax bits: 8 packed code bytes (even element in the low
+// nibble) and one E4M3 scale code.
+//
+// The element quotient q = fl32(w / d) uses one correctly rounded reciprocal y = 1/d per block:
+// q0 = w*y, r = fma(-q0, d, w) (exact), q = fma(r, y, q0) is the correctly rounded quotient when
+// d and y are normal (Markstein's theorem); its sign is copied from w so that -0 stays -0. A block whose d is zero or subnormal falls back to
+// the exact division and the software rounding rule (e2m1_magnitude), as does 0/0 there.
+__device__ __forceinline__ void quantize_block(const uint32_t wp[kBlock / 2], uint32_t amax_bits, uint32_t packed[2],
                                                uint32_t& scale_code) {
   const float ts = tensor_scale_from_amax_bits(amax_bits);
   const float six_ts = 6.0f * ts;
   uint32_t bmax = 0;
 #pragma unroll
-  for (int i = 0; i < kBlock; ++i) bmax = max(bmax, wb[i] & 0x7FFFu);
+  for (int i = 0; i < kBlock / 2; ++i) bmax = max(bmax, max(wp[i] & 0x7FFFu, (wp[i] >> 16) & 0x7FFFu));
   const float bamax = bf16_bits_to_f32(bmax);
   const float sb = (amax_bits == 0u) ? 0.0f : bamax / six_ts;
   const uint32_t S = e4m3_encode_nonneg(sb);
   const float d = e4m3_to_f32(S) * ts;
+  scale_code = S;
+  float w[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock / 2; ++i) {
+    w[2 * i] = bf16_lo(wp[i]);
+    w[2 * i + 1] = bf16_hi(wp[i]);
+  }
   packed[0] = 0u;
   packed[1] = 0u;
+  if (S != 0u && !(d >= 0x1p-126f)) {
 #pragma unroll
-  for (int i = 0; i < kBlock; ++i) {
-    const float w = bf16_bits_to_f32(wb[i]);
-    const uint32_t mag = (S == 0u) ? 0u : e2m1_magnitude(__builtin_fabsf(w / d));
-    const uint32_t code = ((wb[i] >> 12) & 8u) | mag;
-    packed[i >> 3] |= code << (4 * (i & 7));
+    for (int i = 0; i < kBlock; ++i) {
+      const uint32_t sign = (__float_as_uint(w[i]) >> 28) & 8u;
+      packed[i >> 3] |= (sign | e2m1_magnitude(__builtin_fabsf(w[i] / d))) << (4 * (i & 7));
+    }
+    return;
   }
-  scale_code = S;
+  float q[kBlock];
+  if (S == 0u) {
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) q[i] = w[i] * 0.0f;          // magnitude 0, sign of w
+  } else {
+    const float y = 1.0f / d;
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) {
+      const float q0 = w[i] * y;
+      // the correction rounds -0 + +0 to +0: the quotient takes the sign of w explicitly
+      q[i] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, d, w[i]), y, q0), w[i]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    packed[0] = cvt_fp4_pair(packed[0], q[2 * j], q[2 * j + 1], j);
+    packed[1] = cvt_fp4_pair(packed[1], q[8 + 2 * j], q[8 + 2 * j + 1], j);
+  }
 }
 
 // ---------------------------------------------------------------------------------- rank 0
-// Rebuild 16 consecutive elements [col, col+16) of row `row` as bf16 bit patterns (r == 0).
-__device__ __forceinline__ void rebuild_block_r0(const Theta& t, int row, int col, uint32_t wb[kBlock]) {
+// Rebuild 16 consecutive elements [col, col+16) of row `row` as eight packed bf16 pairs (r == 0).
+__device__ __forceinline__ void rebuild_block_r0(const Theta& t, int row, int col, uint32_t wp[kBlock / 2]) {
   const u32x4* src = reinterpret_cast<const u32x4*>(t.W0 + (size_t)row * t.K + col);
   const u32x4 a = __builtin_nontemporal_load(src);
   const u32x4 b = __builtin_nontemporal_load(src + 1);
   const uint32_t w0[kBlock / 2] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   if (t.s == nullptr) {                             // passthrough: W_eff = W0 bit for bit
 #pragma unroll
-    for (int i = 0; i < kBlock / 2; ++i) {
-      wb[2 * i] = w0[i] & 0xFFFFu;
-      wb[2 * i + 1] = w0[i] >> 16;
-    }
+    for (int i = 0; i < kBlock / 2; ++i) wp[i] = w0[i];
     return;
   }
   const float si = bf16_bits_to_f32(t.s[row]);
 #pragma unroll
-  for (int i = 0; i < kBlock / 2; ++i) {             // bf16 x bf16 products are exact in fp32
-    wb[2 * i] = f32_to_bf16_bits(si * bf16_bits_to_f32(w0[i] & 0xFFFFu));
-    wb[2 * i + 1] = f32_to_bf16_bits(si * bf16_bits_to_f32(w0[i] >> 16));
-  }
+  for (int i = 0; i < kBlock / 2; ++i)              // bf16 x bf16 products are exact in fp32
+    wp[i] = pack_bf16(si * bf16_lo(w0[i]), si * bf16_hi(w0[i]));
+}
+
+// Fold the |w| bit patterns of eight packed bf16 pairs into a running max (as fp32 bit patterns;
+// NaN patterns sort above +inf).
+__device__ __forceinline__ uint32_t amax_bits_of(const uint32_t wp[kBlock / 2], uint32_t m) {
+#pragma unroll
+  for (int i = 0; i < kBlock / 2; ++i) m = max(m, max((wp[i] << 16) & 0x7FFF0000u, wp[i] & 0x7FFF0000u));
+  return m;
 }
 
 __global__ __launch_bounds__(256) void k_reconstruct_r0(Theta t, uint16_t* __restrict__ out, int64_t nblocks) {
@@ -84,13 +141,11 @@ __global__ __launch_bounds__(256) void k_reconstruct_r0(Theta t, uint16_t* __res
   if (b >= nblocks) return;
   const int bpr = t.K / kBlock;
   const int row = (int)(b / bpr), col = (int)(b % bpr) * kBlock;
-  uint32_t wb[kBlock];
-  rebuild_block_r0(t, row, col, wb);
-  u32x4 lo = {wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16), wb[4] | (wb[5] << 16), wb[6] | (wb[7] << 16)};
-  u32x4 hi = {wb[8] | (wb[9] << 16), wb[10] | (wb[11] << 16), wb[12] | (wb[13] << 16), wb[14] | (wb[15] << 16)};
+  uint32_t wp[kBlock / 2];
+  rebuild_block_r0(t, row, col, wp);
   u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)row * t.K + col);
-  dst[0] = lo;
-  dst[1] = hi;
+  dst[0] = u32x4{wp[0], wp[1], wp[2], wp[3]};
+  dst[1] = u32x4{wp[4], wp[5], wp[6], wp[7]};
 }
 
 __global__ void k_zero_slot(uint32_t* slot) {
@@ -115,10 +170,9 @@ __global__ __launch_bounds__(256) void k_amax_r0(Theta t, uint32_t* slot, int64_
   const int bpr = t.K / kBlock;
   for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * 256) {
     const int row = (int)(b / bpr), col = (int)(b % bpr) * kBlock;
-    uint32_t wb[kBlock];
-    rebuild_block_r0(t, row, col, wb);
-#pragma unroll
-    for (int i = 0; i < kBlock; ++i) m = max(m, (wb[i] & 0x7FFFu) << 16);
+    uint32_t wp[kBlock / 2];
+    rebuild_block_r0(t, row, col, wp);
+    m = amax_bits_of(wp, m);
   }
   fold_amax(m, slot);
 }
@@ -137,10 +191,10 @@ __global__ __launch_bounds__(256) void k_quantize_r0(Theta t, const uint32_t* __
     *sdst = 0x7F;
     return;
   }
-  uint32_t wb[kBlock];
-  rebuild_block_r0(t, row, cb * kBlock, wb);
+  uint32_t wp[kBlock / 2];
+  rebuild_block_r0(t, row, cb * kBlock, wp);
   uint32_t packed[2], S;
-  quantize_block(wb, amax_bits, packed, S);
+  quantize_block(wp, amax_bits, packed, S);
   *cdst = u32x2{packed[0], packed[1]};
   *sdst = (uint8_t)S;
 }
@@ -268,32 +322,26 @@ __global__ __launch_bounds__(256) void k_lowrank_tile(Theta t, uint32_t* slot, u
 #pragma unroll
   for (int rr = 0; rr < kRowsPerThread; ++rr) {
     const uint32_t ww[8] = {w0a[rr].x, w0a[rr].y, w0a[rr].z, w0a[rr].w, w0b[rr].x, w0b[rr].y, w0b[rr].z, w0b[rr].w};
-    uint32_t wb[kBlock];
+    uint32_t wp[kBlock / 2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      wb[2 * i] = f32_to_bf16_bits(__builtin_fmaf(si[rr], bf16_bits_to_f32(ww[i] & 0xFFFFu), acc[rr][2 * i]));
-      wb[2 * i + 1] = f32_to_bf16_bits(__builtin_fmaf(si[rr], bf16_bits_to_f32(ww[i] >> 16), acc[rr][2 * i + 1]));
-    }
+    for (int i = 0; i < 8; ++i)
+      wp[i] = pack_bf16(__builtin_fmaf(si[rr], bf16_lo(ww[i]), acc[rr][2 * i]),
+                        __builtin_fmaf(si[rr], bf16_hi(ww[i]), acc[rr][2 * i + 1]));
     const bool ok = col_ok && rows[rr] < t.N;
     if (PASS == kPassAmax) {
-      if (ok) {
-#pragma unroll
-        for (int i = 0; i < kBlock; ++i) m = max(m, (wb[i] & 0x7FFFu) << 16);
-      }
+      if (ok) m = amax_bits_of(wp, m);
     } else if (PASS == kPassQuantize) {
       if (ok) {
         uint32_t packed[2], S;
-        quantize_block(wb, amax_bits, packed, S);
+        quantize_block(wp, amax_bits, packed, S);
         *reinterpret_cast<u32x2*>(codes + (size_t)rows[rr] * (t.K / 2) + col / 2) = u32x2{packed[0], packed[1]};
         scales[(size_t)rows[rr] * (t.K / kBlock) + col / kBlock] = (uint8_t)S;
       }
     } else {
       if (ok) {
-        u32x4 lo = {wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16), wb[4] | (wb[5] << 16), wb[6] | (wb[7] << 16)};
-        u32x4 hi = {wb[8] | (wb[9] << 16), wb[10] | (wb[11] << 16), wb[12] | (wb[13] << 16), wb[14] | (wb[15] << 16)};
         u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)rows[rr] * t.K + col);
-        dst[0] = lo;
-        dst[1] = hi;
+        dst[0] = u32x4{wp[0], wp[1], wp[2], wp[3]};
+        dst[1] = u32x4{wp[4], wp[5], wp[6], wp[7]};
       }
     }
   }

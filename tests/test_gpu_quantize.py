@@ -68,6 +68,9 @@ def _adversarial(seed, n, K, scale=0.02):
     w[0, 32:48] = -0.0
     w[1, :16] = np.float32(1e-4 * scale) * g.standard_normal(16)
     w[1, 16:32] = np.linspace(-1, 1, 16) * scale
+    w[1, 32:48] = g.standard_normal(16) * scale      # signed zeros inside a block with a non-zero scale
+    w[1, 33] = -0.0
+    w[1, 35] = 0.0
     w[2, :] = g.choice([-1, 1], K) * np.exp2(g.integers(-30, 0, K)) * scale
     # exact E2M1 midpoints relative to the block step of a block whose bamax sits at 448 * 6 * ts
     return O.f32_to_bf16_rne(w)
