@@ -12,6 +12,11 @@ own workload -- all 410 theta bundles at rank 16 with s ~ U(0.9, 1.1) (420 segme
 quantizations: in 10 layers k's bundle also fills the v rows) -- and so is the small-M verify
 product (M = 4 and 8) on one layer; both are reported as extra fields.
 
+Two more token streams are timed the same way and reported under "streams": the chained token
+in which each layer's gate|up launch applies the activation epilogue (attnq_gemv_nvfp4_glu)
+and its down projection reads that bf16 output, and the coverage-matched mix with the attention
+projections left in bf16 (attnq_gemv_bf16) and the MLP in NVFP4.
+
 Output: one JSON line (see the design doc for the fields). Options:
   --steps K --warmup W       timed / untimed steps (defaults 20 / 5)
   --gpus N                   only N = 1 is supported (one GPU)
@@ -94,6 +99,9 @@ class Model:
         self.lm_head = inputs.device_normal_bf16((VOCAB, HIDDEN), 0.02, seed=7, device=dev)
         self.x_head = torch.randn(HIDDEN, device=dev, generator=torch.Generator(device=dev).manual_seed(8)).to(torch.bfloat16)
         self.y_head = torch.empty(VOCAB, dtype=torch.float32, device=dev)
+        # gate|up activation output per layer (the input of down in the chained stream)
+        self.h = [torch.empty(GU_SEGS[0], dtype=torch.bfloat16, device=dev) for _ in range(N_LAYERS)]
+        self.attn_bf16 = None
 
     def quantize_passthrough(self, dev):
         """Fill every NVFP4 weight from a seeded device bf16 W0 (passthrough reconstruction)."""
@@ -115,6 +123,59 @@ class Model:
                 W, x, y, _, _ = lay[name]
                 A.attnq_gemv_nvfp4(W, x, y)
         A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
+
+    def glu_step(self):
+        """The token with the gate|up epilogue: gate|up writes h = gelu_tanh(gate) * up (bf16), and
+        down reads h, so each layer's down projection depends on its gate|up output."""
+        A = self.A
+        for L, lay in enumerate(self.layers):
+            for name in ("qkv", "o"):
+                W, x, y, _, _ = lay[name]
+                A.attnq_gemv_nvfp4(W, x, y)
+            W, x, _, _, _ = lay["gate_up"]
+            A.attnq_gemv_nvfp4_glu(W, x, A.ACT_GELU_TANH, self.h[L])
+            W, _, y, _, _ = lay["down"]
+            A.attnq_gemv_nvfp4(W, self.h[L], y)
+        A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
+
+    def build_bf16_attention(self, dev):
+        """bf16 q|k|v and o weights for every layer (the mixed stream: attention left in bf16)."""
+        from nvfp4_weight_only_rtn_amd import inputs
+        self.attn_bf16 = []
+        for L in range(N_LAYERS):
+            qkv = inputs.device_normal_bf16((sum(QKV_SEGS), HIDDEN), 0.02, seed=70_000 + 2 * L, device=dev)
+            o = inputs.device_normal_bf16(O_SHAPE, 0.02, seed=70_001 + 2 * L, device=dev)
+            self.attn_bf16.append((qkv, o))
+
+    def mixed_step(self):
+        """Attention projections in bf16, MLP in NVFP4 (the pages' coverage-matched mix), tied bf16 head."""
+        A = self.A
+        for L, lay in enumerate(self.layers):
+            qkv, o = self.attn_bf16[L]
+            A.attnq_gemv_bf16(qkv, lay["qkv"][1], lay["qkv"][2])
+            A.attnq_gemv_bf16(o, lay["o"][1], lay["o"][2])
+            for name in ("gate_up", "down"):
+                W, x, y, _, _ = lay[name]
+                A.attnq_gemv_nvfp4(W, x, y)
+        A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
+
+    def glu_bytes_per_step(self) -> int:
+        total = 0
+        for lay in self.layers:
+            for name in PROJ_NAMES:
+                W, _, _, segs, K = lay[name]
+                total += nvfp4_bytes(W.N, K, len(segs))
+            total -= 4 * GU_SEGS[0] * 2 - 2 * GU_SEGS[0]      # h (bf16 F) written instead of y (fp32 2F)
+        return total + bf16_bytes(VOCAB, HIDDEN)
+
+    def mixed_bytes_per_step(self) -> int:
+        total = 0
+        for lay in self.layers:
+            for name in ("gate_up", "down"):
+                W, _, _, segs, K = lay[name]
+                total += nvfp4_bytes(W.N, K, len(segs))
+            total += bf16_bytes(sum(QKV_SEGS), HIDDEN) + bf16_bytes(O_SHAPE[0], O_SHAPE[1])
+        return total + bf16_bytes(VOCAB, HIDDEN)
 
     def bytes_per_step(self) -> int:
         total = 0
@@ -139,6 +200,24 @@ def time_steps(fn, steps: int) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def graph_timing(fn, warmup: int, steps: int) -> float:
+    """ms per step of `fn` captured once as a hipGraph and replayed."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(max(1, warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = time_steps(graph.replay, steps)
+    del graph
+    return ms
 
 
 def dominant_kernel_timing(model: Model, reps: int):
@@ -362,6 +441,24 @@ def main():
     dom_bytes = nvfp4_bytes(W_gu.N, W_gu.K, 2)
     achieved = dom_bytes / (dom_mean * 1e-3) / 1e9
 
+    log("timing the chained stream (gate|up epilogue feeds down) and the bf16-attention mix")
+    glu_ms = graph_timing(model.glu_step, args.warmup, args.steps)
+    glu_bytes = model.glu_bytes_per_step()
+    model.build_bf16_attention(dev)
+    mixed_ms = graph_timing(model.mixed_step, args.warmup, args.steps)
+    mixed_bytes = model.mixed_bytes_per_step()
+    model.attn_bf16 = None
+    torch.cuda.empty_cache()
+    streams = {
+        "glu_chained": {"what": "gate|up GEMV with the gelu-tanh epilogue writing bf16 h, down reading h",
+                        "ms_per_token": round(glu_ms, 5), "bytes_per_token": glu_bytes,
+                        "TBps": round(glu_bytes / (glu_ms * 1e-3) / 1e12, 4)},
+        "bf16_attention": {"what": "q|k|v and o in bf16 (attnq_gemv_bf16), gate|up and down NVFP4, bf16 lm_head",
+                           "ms_per_token": round(mixed_ms, 5), "bytes_per_token": mixed_bytes,
+                           "TBps": round(mixed_bytes / (mixed_ms * 1e-3) / 1e12, 4)},
+    }
+    log(f"streams: {streams}")
+
     small_m = small_m_timing(A, model, max(3, args.steps // 4))
     if args.calibrate_copy:
         calibrate_copy(dev)
@@ -396,6 +493,7 @@ def main():
                      "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_mean * 1e3, 3),
                      "launches_timed": dom_n},
         "small_m": small_m,
+        "streams": streams,
         "load_path": load,
     }
     if not args.no_cpu_baseline:

@@ -128,6 +128,29 @@ ATTNQ_API attnq_status attnq_quantize_nvfp4(const attnq_theta* theta, const attn
 ATTNQ_API attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y,
                               attnq_stream stream);
 
+/* Activations of the gate|up epilogue (attnq_gemv_nvfp4_glu). The pages do not name the model's
+ * activation, so it is a parameter:
+ *   GELU_TANH: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)))
+ *   SILU:      g / (1 + exp(-g))
+ *   IDENTITY:  g (the plain product gate * up) */
+#define ATTNQ_ACT_GELU_TANH 0
+#define ATTNQ_ACT_SILU 1
+#define ATTNQ_ACT_IDENTITY 2
+
+/* Fused gate|up projection with its activation, the input of the down projection
+ * (weightless "GPU and cache acceleration", "Future work": gate/up fusion on the pattern of the
+ * Q/K/V fusion). W holds two segments of F = N/2 rows each, gate rows then up rows
+ * (seg_end = {F, N}). For j < F:
+ *   g_j = sum_k x[k] * weight[j][k],  u_j = sum_k x[k] * weight[F + j][k]   (fp32, as in
+ *         attnq_gemv_nvfp4, whose y[j] and y[F + j] they equal bit for bit),
+ *   h[j] = bf16_rne(fl32(act(g_j) * u_j)), the activation evaluated in fp32.
+ * One kernel, no fp32 y round trip. x [K] bf16 16-byte aligned; h [F] bf16 2-byte aligned, must
+ * not overlap x or the weight.
+ * Errors: as attnq_gemv_nvfp4; ATTNQ_ERR_SEGMENT unless n_seg == 2 and seg_end[0] * 2 == N;
+ * ATTNQ_ERR_SHAPE for an unknown act. */
+ATTNQ_API attnq_status attnq_gemv_nvfp4_glu(const attnq_nvfp4* W, const uint16_t* x, int32_t act, uint16_t* h,
+                                  attnq_stream stream);
+
 /* y[n] = sum_k x[k] * W[n][k] for a bf16 weight [N][K] (the tied lm_head, or projections
  * left in bf16). W and x 16-byte aligned, y 4-byte aligned. fp32 accumulation. */
 ATTNQ_API attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, const uint16_t* x, float* y,

@@ -15,6 +15,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnq.so")
 MAX_SEGMENTS = 4
 LAYOUT_ROW_MAJOR = 0
+ACT_GELU_TANH, ACT_SILU, ACT_IDENTITY = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m nvfp4_weight_only_rtn_amd.build` "
@@ -41,6 +42,7 @@ _SIGS = {
     "attnq_reconstruct": [ctypes.POINTER(_Theta), _P, _P],
     "attnq_quantize_nvfp4": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), _I, _P],
     "attnq_gemv_nvfp4": [ctypes.POINTER(_NVFP4), _P, _P, _P],
+    "attnq_gemv_nvfp4_glu": [ctypes.POINTER(_NVFP4), _P, _I, _P, _P],
     "attnq_gemv_bf16": [_P, _I, _I, _P, _P, _P],
     "attnq_gemm_nvfp4_small_m": [ctypes.POINTER(_NVFP4), _P, _I, _I, _P, _I, _P],
 }
@@ -126,6 +128,10 @@ def attnq_quantize_nvfp4(W0, s, U, V, dst: NVFP4Weight, seg: int = 0, stream=Non
 
 def attnq_gemv_nvfp4(W: NVFP4Weight, x, y, stream=None) -> None:
     _check(_lib.attnq_gemv_nvfp4(ctypes.byref(W.desc()), _ptr(x, 2), _ptr(y, 4), _stream(stream)))
+
+
+def attnq_gemv_nvfp4_glu(W: NVFP4Weight, x, act: int, h, stream=None) -> None:
+    _check(_lib.attnq_gemv_nvfp4_glu(ctypes.byref(W.desc()), _ptr(x, 2), act, _ptr(h, 2), _stream(stream)))
 
 
 def attnq_gemv_bf16(W, x, y, stream=None) -> None:

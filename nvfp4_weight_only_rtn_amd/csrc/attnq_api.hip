@@ -78,6 +78,17 @@ attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y,
   return from_hip(attnq::launch_gemv_nvfp4(*W, x, y, static_cast<hipStream_t>(stream)));
 }
 
+attnq_status attnq_gemv_nvfp4_glu(const attnq_nvfp4* W, const uint16_t* x, int32_t act, uint16_t* h,
+                                  attnq_stream stream) {
+  attnq_status st = check_nvfp4(W);
+  if (st != ATTNQ_OK) return st;
+  if (W->n_seg != 2 || W->seg_end[0] * 2 != W->N) return ATTNQ_ERR_SEGMENT;
+  if (act != ATTNQ_ACT_GELU_TANH && act != ATTNQ_ACT_SILU && act != ATTNQ_ACT_IDENTITY) return ATTNQ_ERR_SHAPE;
+  if (x == nullptr || (h == nullptr && W->N != 0)) return ATTNQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(h, 2)) return ATTNQ_ERR_ALIGN;
+  return from_hip(attnq::launch_gemv_nvfp4_glu(*W, x, act, h, static_cast<hipStream_t>(stream)));
+}
+
 attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, const uint16_t* x, float* y, attnq_stream stream) {
   if (N < 0 || K <= 0 || K % 32 != 0) return ATTNQ_ERR_SHAPE;
   if (x == nullptr || ((W == nullptr || y == nullptr) && N != 0)) return ATTNQ_ERR_NULL;

@@ -50,16 +50,39 @@ __device__ __forceinline__ float chunk_dot(const u32x4 cv, uint32_t sv, const ui
   return acc;
 }
 
-template <int R, int KSPLIT>
+// Epilogue of the gate|up projection with its activation (the input of down): row pair
+// (j, F + j) of a fused [gate; up] weight gives h[j] = bf16(act(gate_j) * up_j), computed in fp32.
+__device__ __forceinline__ float activation(float g, int act) {
+  if (act == ATTNQ_ACT_GELU_TANH) {
+    const float inner = 0.7978845608028654f * (g + 0.044715f * g * g * g);   // sqrt(2/pi)
+    return 0.5f * g * (1.0f + tanhf(inner));
+  }
+  if (act == ATTNQ_ACT_SILU) return g / (1.0f + expf(-g));
+  return g;                                                                   // ATTNQ_ACT_IDENTITY
+}
+
+__device__ __forceinline__ void store_glu(uint16_t* h, int j, float g, float u, int act) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v p = {(__bf16)(activation(g, act) * u), (__bf16)0.0f};
+  h[j] = (uint16_t)(__builtin_bit_cast(uint32_t, p) & 0xFFFFu);
+}
+
+// EPI 0 stores y; EPI 1 is the gate|up epilogue: R == 2, the wave's two rows are j and F + j of a
+// two-segment weight (F = N / 2) and it stores h[j] (bf16) instead of y.
+template <int R, int KSPLIT, int EPI = 0>
 __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                                     const float* __restrict__ tensor_scale, SegTable segs,
-                                                    const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K) {
+                                                    const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K,
+                                                    uint16_t* __restrict__ h = nullptr, int act = 0) {
   static_assert(4 % KSPLIT == 0, "K split must divide the 4 waves of a workgroup");
+  static_assert(EPI == 0 || (R == 2 && KSPLIT == 1), "the gate|up epilogue takes one row pair per wave");
   constexpr int kRowGroups = 4 / KSPLIT;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rg = wave / KSPLIT, ks = wave % KSPLIT;
   const int row0 = (blockIdx.x * kRowGroups + rg) * R;
+  const int F = N >> 1, pj = blockIdx.x * kRowGroups + rg;       // EPI 1: pair index
+  auto row_of = [&](int r) { return EPI ? min(pj, F - 1) + r * F : min(row0 + r, N - 1); };
   const int cpr = K >> 5;
   const int slice = (cpr + KSPLIT - 1) / KSPLIT;
   const int c_begin = ks * slice;
@@ -80,7 +103,7 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
     uint32_t sv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = min(row0 + r, N - 1);          // clamp: rows past N load row N-1, result discarded
+      const int row = row_of(r);                     // clamp: rows past N load row N-1, result discarded
       cv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + row * code_pitch) + c);
       sv[r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
     }
@@ -91,7 +114,9 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
 
-  if constexpr (KSPLIT == 1) {
+  if constexpr (EPI == 1) {
+    if (lane == 0 && pj < F) store_glu(h, pj, acc[0] * tensor_scale[0], acc[1] * tensor_scale[1], act);
+  } else if constexpr (KSPLIT == 1) {
     if (lane < R) {
       float v = acc[0];
 #pragma unroll
@@ -122,20 +147,24 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 // four 16-byte quarter reads of a chunk ([q][chunk]) are each bank-conflict free. XFIRST issues
 // the x loads (at most XI 16-byte pieces per thread) before the weight loads, so the LDS staging
 // waits for x only; otherwise x is loaded after the weights (better for the tall gate|up shape).
-template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1>
+template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1, int EPI = 0>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t* __restrict__ codes,
                                                                    const uint8_t* __restrict__ scales,
                                                                    const float* __restrict__ tensor_scale, SegTable segs,
                                                                    const uint16_t* __restrict__ x, float* __restrict__ y,
-                                                                   int N, int K) {
+                                                                   int N, int K, uint16_t* __restrict__ h = nullptr,
+                                                                   int act = 0) {
   static_assert(WAVES % KSPLIT == 0, "K split must divide the waves of a workgroup");
   static_assert(!XFIRST || XL, "x-first staging is an LDS staging");
+  static_assert(EPI == 0 || (R == 2 && KSPLIT == 1), "the gate|up epilogue takes one row pair per wave");
   extern __shared__ u32x4 xs[];
   constexpr int kRowGroups = WAVES / KSPLIT;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rg = wave / KSPLIT, ks = wave % KSPLIT;
   const int row0 = (blockIdx.x * kRowGroups + rg) * R;
+  const int F = N >> 1, pj = blockIdx.x * kRowGroups + rg;       // EPI 1: pair index
+  auto row_of = [&](int r) { return EPI ? min(pj, F - 1) + r * F : min(row0 + r, N - 1); };
   const int cpr = K >> 5;
   const int slice = (cpr + KSPLIT - 1) / KSPLIT;
   const int c_begin = ks * slice;
@@ -156,7 +185,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
     const int c = min(c_begin + s * 64 + lane, cpr - 1);       // clamped: lanes past the slice reload a valid chunk
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = min(row0 + r, N - 1);
+      const int row = row_of(r);
       cv[s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + row * code_pitch) + c);
       sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
     }
@@ -194,7 +223,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
-  if constexpr (KSPLIT == 1) {
+  if constexpr (EPI == 1) {
+    if (lane == 0 && pj < F) store_glu(h, pj, acc[0] * tensor_scale[0], acc[1] * tensor_scale[1], act);
+  } else if constexpr (KSPLIT == 1) {
     if (lane < R) {
       float v = acc[0];
 #pragma unroll
@@ -266,6 +297,12 @@ SegTable seg_table(const attnq_nvfp4& W) {
   return t;
 }
 
+void launch_glu_loop(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, int act, hipStream_t stream) {
+  const unsigned grid = (unsigned)((W.N / 2 + 3) / 4);
+  k_gemv_nvfp4<2, 1, 1><<<grid, 256, 0, stream>>>(W.codes, W.scales, W.tensor_scale, seg_table(W), x, nullptr, W.N,
+                                                  W.K, h, act);
+}
+
 template <int R, int KSPLIT>
 void launch_nvfp4_loop(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
   constexpr int rows_per_wg = R * (4 / KSPLIT);
@@ -280,6 +317,14 @@ void launch_nvfp4_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, hip
   const size_t lds = XL ? (size_t)W.K * 2 : 0;
   k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI><<<grid, 64 * WAVES, lds, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
+}
+
+// gate|up epilogue launches: one row pair per wave, F = N / 2 pairs
+template <int S>
+void launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, int act, hipStream_t stream) {
+  const unsigned grid = (unsigned)((W.N / 2 + 7) / 8);
+  k_gemv_nvfp4_oneshot<2, 1, S, true, 8, false, 1, 1><<<grid, 512, (size_t)W.K * 2, stream>>>(
+      W.codes, W.scales, W.tensor_scale, seg_table(W), x, nullptr, W.N, W.K, h, act);
 }
 
 }  // namespace
@@ -302,6 +347,22 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
     launch_nvfp4_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 2 x 512 >= K/8)
   else
     launch_nvfp4_loop<2, 2>(W, x, y, stream);
+  return hipGetLastError();
+}
+
+// gate|up with its activation: the one-shot kernel stages x in LDS for rows of up to 6144
+// elements (the fused gate|up shapes); longer rows walk K in the loop kernel.
+hipError_t launch_gemv_nvfp4_glu(const attnq_nvfp4& W, const uint16_t* x, int act, uint16_t* h, hipStream_t stream) {
+  if (W.N == 0) return hipSuccess;
+  const int cpr = W.K / 32;
+  if (cpr <= 64)
+    launch_glu_oneshot<1>(W, x, h, act, stream);
+  else if (cpr <= 128)
+    launch_glu_oneshot<2>(W, x, h, act, stream);
+  else if (cpr <= 192)
+    launch_glu_oneshot<3>(W, x, h, act, stream);
+  else
+    launch_glu_loop(W, x, h, act, stream);
   return hipGetLastError();
 }
 

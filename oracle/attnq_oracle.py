@@ -23,6 +23,14 @@ What it computes, and where each step is defined:
   acceleration", "Where GPU time goes" (weight-reading GEMVs, no dequant
   kernel) and "Throughput", "The NVFP4 MLP kernels are the least
   bandwidth-efficient on the step".
+* The fused gate|up projection with its activation, ``h = act(gate) * up``
+  rounded to bf16 as the input of the down projection -- weightless "GPU and
+  cache acceleration", "Future work" (gate/up fusion on the Q/K/V pattern).
+  The pages do not name the activation; GELU with the tanh approximation,
+  SiLU and the identity are offered. Reading: the activation and product are
+  evaluated in float64 on the float64 GEMV outputs and rounded once to bf16
+  (PARITY PINNED by closed forms, odd-part identities and a library
+  cross-check in tests/test_oracle_glu.py).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -81,6 +89,19 @@ def f32_to_bf16_rne(a: np.ndarray) -> np.ndarray:
     nan = np.isnan(a)
     out = np.where(nan, upper | np.uint64(0x0040), out)
     return out.astype(np.uint16)
+
+
+def f64_to_bf16_rne(a: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bits with one round-to-nearest-even step. The float32 intermediate is
+    rounded to odd (truncate toward zero, then set the last bit if anything was dropped), which
+    keeps the second rounding exact because float32 carries 16 more bits than bf16."""
+    a = np.asarray(a, dtype=np.float64)
+    t = a.astype(np.float32)
+    away = np.abs(t.astype(np.float64)) > np.abs(a)
+    t = np.where(away, np.nextafter(t, np.float32(0)), t).astype(np.float32)
+    inexact = t.astype(np.float64) != a
+    bits = t.view(np.uint32) | np.where(inexact & np.isfinite(a), np.uint32(1), np.uint32(0))
+    return f32_to_bf16_rne(bits.astype(np.uint32).view(np.float32))
 
 
 # ---------------------------------------------------------------------------
@@ -336,3 +357,39 @@ def abs_dot_bf16(W_bf16, x_bf16, rows=None) -> np.ndarray:
     x = np.abs(bf16_to_f32(x_bf16).astype(np.float64)).reshape(-1)
     W = np.asarray(W_bf16) if rows is None else np.asarray(W_bf16)[rows]
     return np.abs(bf16_to_f32(W).astype(np.float64)) @ x
+
+
+# ---------------------------------------------------------------------------
+# gate|up epilogue: h = act(gate) * up, the input of the down projection
+# ---------------------------------------------------------------------------
+ACT_GELU_TANH, ACT_SILU, ACT_IDENTITY = 0, 1, 2
+
+
+def activation(g: np.ndarray, act: int) -> np.ndarray:
+    """The epilogue activation in float64: GELU with the tanh approximation
+    0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))), SiLU g / (1 + exp(-g)), or the identity."""
+    g = np.asarray(g, dtype=np.float64)
+    if act == ACT_GELU_TANH:
+        return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+    if act == ACT_SILU:
+        return g / (1.0 + np.exp(-g))
+    if act == ACT_IDENTITY:
+        return g
+    raise ValueError(f"unknown activation {act}")
+
+
+def glu(y_gate: np.ndarray, y_up: np.ndarray, act: int) -> np.ndarray:
+    """h[j] = bf16(act(gate[j]) * up[j]): float64 arithmetic, one rounding to bf16 (bits)."""
+    return f64_to_bf16_rne(activation(y_gate, act) * np.asarray(y_up, dtype=np.float64))
+
+
+def gemv_nvfp4_glu(codes, scales, ts, x_bf16, rows=None) -> np.ndarray:
+    """The fused gate|up projection of a two-segment weight [gate; up] (F rows each) followed by
+    the epilogue: returns (gate, up) float64 GEMV outputs for the pair rows `rows` (default all)."""
+    N = np.asarray(codes).shape[0]
+    F = N // 2
+    j = np.arange(F) if rows is None else np.asarray(rows)
+    seg_end = [F, N]
+    g = gemv_nvfp4(codes, scales, ts, x_bf16, seg_end, rows=j)
+    u = gemv_nvfp4(codes, scales, ts, x_bf16, seg_end, rows=j + F)
+    return g, u

@@ -131,6 +131,16 @@ def test_gemv_and_gemm_validation():
     assert lib.attnq_gemv_bf16(FAKE, -1, 64, FAKE, FAKE, None) == 2
     assert lib.attnq_gemv_bf16(None, 10, 64, FAKE, FAKE, None) == 1
     assert lib.attnq_gemv_bf16(FAKE + 4, 10, 64, FAKE, FAKE, None) == 3
+    glu = lib.attnq_gemv_nvfp4_glu
+    pair = _nv(N=64, n_seg=2, seg_end=[32, 64])
+    assert glu(ctypes.byref(nv), FAKE, 0, FAKE, None) == 4                        # one segment
+    assert glu(ctypes.byref(_nv(N=64, n_seg=2, seg_end=[16, 64])), FAKE, 0, FAKE, None) == 4  # unequal halves
+    assert glu(ctypes.byref(pair), FAKE, 3, FAKE, None) == 2                      # unknown activation
+    assert glu(ctypes.byref(pair), FAKE, -1, FAKE, None) == 2
+    assert glu(ctypes.byref(pair), None, 0, FAKE, None) == 1
+    assert glu(ctypes.byref(pair), FAKE, 0, None, None) == 1
+    assert glu(ctypes.byref(pair), FAKE + 8, 0, FAKE, None) == 3
+    assert glu(ctypes.byref(pair), FAKE, 1, FAKE + 1, None) == 3                  # h needs 2-byte alignment
     g = lib.attnq_gemm_nvfp4_small_m
     assert g(ctypes.byref(nv), FAKE, 17, 64, FAKE, 64, None) == 2                 # M > 16
     assert g(ctypes.byref(nv), FAKE, 4, 32, FAKE, 64, None) == 2                  # ldx < K
