@@ -151,6 +151,23 @@ ATTNQ_API attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x,
 ATTNQ_API attnq_status attnq_gemv_nvfp4_glu(const attnq_nvfp4* W, const uint16_t* x, int32_t act, uint16_t* h,
                                   attnq_stream stream);
 
+/* Runtime low-rank product over a shared NVFP4 block, the weight never rebuilt:
+ *   y[n] = s[n] * (sum_k x[k] * weight0[n][k]) + sum_j U[n][j] * t[j],  t[j] = sum_k x[k] * V[k][j]
+ * ("Throughput", "The runtime reconstruction path does not reach dense parity": W0 and the
+ * low-rank delta applied on every forward pass; weightless "GPU and cache acceleration",
+ * "Architecture decisions / Custom-op kernel": the W0 dot product and the low-rank delta fused in
+ * one kernel with nothing materialized; "Future work / Trained weight sharing": a shared NVFP4 W0
+ * plus a bf16 low-rank pair). W0 is an NVFP4 weight [N][K] that several projections may share
+ * (each call reads it once); s [N] bf16 or NULL (s = 1); U [N][r], V [K][r] bf16 row-major,
+ * NULL when r == 0 (U may also be NULL when N == 0), 0 <= r <= 64. t is a caller-owned fp32 workspace of r values that receives
+ * V^T x (NULL iff r == 0). Two kernels in stream order: t (one workgroup, fixed summation order),
+ * then the streaming GEMV whose epilogue applies s and U t. fp32 arithmetic throughout.
+ * x 16-byte aligned, y and t 4-byte aligned, s / U / V 2-byte aligned; y must not overlap the
+ * inputs. Errors: as attnq_gemv_nvfp4; r outside [0, 64] is ATTNQ_ERR_SHAPE. */
+ATTNQ_API attnq_status attnq_gemv_nvfp4_lowrank(const attnq_nvfp4* W0, const uint16_t* s, const uint16_t* U,
+                                      const uint16_t* V, int32_t r, const uint16_t* x, float* t, float* y,
+                                      attnq_stream stream);
+
 /* y[n] = sum_k x[k] * W[n][k] for a bf16 weight [N][K] (the tied lm_head, or projections
  * left in bf16). W and x 16-byte aligned, y 4-byte aligned. fp32 accumulation. */
 ATTNQ_API attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, const uint16_t* x, float* y,

@@ -43,6 +43,7 @@ _SIGS = {
     "attnq_quantize_nvfp4": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), _I, _P],
     "attnq_gemv_nvfp4": [ctypes.POINTER(_NVFP4), _P, _P, _P],
     "attnq_gemv_nvfp4_glu": [ctypes.POINTER(_NVFP4), _P, _I, _P, _P],
+    "attnq_gemv_nvfp4_lowrank": [ctypes.POINTER(_NVFP4), _P, _P, _P, _I, _P, _P, _P, _P],
     "attnq_gemv_bf16": [_P, _I, _I, _P, _P, _P],
     "attnq_gemm_nvfp4_small_m": [ctypes.POINTER(_NVFP4), _P, _I, _I, _P, _I, _P],
 }
@@ -132,6 +133,12 @@ def attnq_gemv_nvfp4(W: NVFP4Weight, x, y, stream=None) -> None:
 
 def attnq_gemv_nvfp4_glu(W: NVFP4Weight, x, act: int, h, stream=None) -> None:
     _check(_lib.attnq_gemv_nvfp4_glu(ctypes.byref(W.desc()), _ptr(x, 2), act, _ptr(h, 2), _stream(stream)))
+
+
+def attnq_gemv_nvfp4_lowrank(W0: NVFP4Weight, s, U, V, x, t, y, stream=None) -> None:
+    r = 0 if U is None else U.shape[1]
+    _check(_lib.attnq_gemv_nvfp4_lowrank(ctypes.byref(W0.desc()), _ptr(s, 2), _ptr(U, 2), _ptr(V, 2), r, _ptr(x, 2),
+                                         _ptr(t, 4), _ptr(y, 4), _stream(stream)))
 
 
 def attnq_gemv_bf16(W, x, y, stream=None) -> None:

@@ -67,22 +67,40 @@ __device__ __forceinline__ void store_glu(uint16_t* h, int j, float g, float u, 
   h[j] = (uint16_t)(__builtin_bit_cast(uint32_t, p) & 0xFFFFu);
 }
 
-// EPI 0 stores y; EPI 1 is the gate|up epilogue: R == 2, the wave's two rows are j and F + j of a
+// Runtime low-rank epilogue (EPI 2): y[row] = s[row] * (x . weight0[row]) + sum_k U[row][k] t[k],
+// with t = V^T x computed beforehand by k_lowrank_t.
+struct LowRank {
+  const uint16_t* s;   // [N] bf16 or null (s = 1)
+  const uint16_t* U;   // [N][r] bf16
+  const float* t;      // [r] fp32
+  int r;
+};
+
+__device__ __forceinline__ float finish_row(float v, float ts, int row, const LowRank& lr) {
+  v *= ts;
+  if (lr.s) v *= bf16_bits_to_f32(lr.s[row]);
+  float d = 0.0f;
+  const uint16_t* u = lr.U + (size_t)row * lr.r;
+  for (int k = 0; k < lr.r; ++k) d = __builtin_fmaf(bf16_bits_to_f32(u[k]), lr.t[k], d);
+  return v + d;
+}
+
+// EPI 0 stores y; EPI 2 stores the low-rank epilogue's y; EPI 1 is the gate|up epilogue: R == 2, the wave's two rows are j and F + j of a
 // two-segment weight (F = N / 2) and it stores h[j] (bf16) instead of y.
 template <int R, int KSPLIT, int EPI = 0>
 __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                                     const float* __restrict__ tensor_scale, SegTable segs,
                                                     const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K,
-                                                    uint16_t* __restrict__ h = nullptr, int act = 0) {
+                                                    uint16_t* __restrict__ h = nullptr, int act = 0, LowRank lr = {}) {
   static_assert(4 % KSPLIT == 0, "K split must divide the 4 waves of a workgroup");
-  static_assert(EPI == 0 || (R == 2 && KSPLIT == 1), "the gate|up epilogue takes one row pair per wave");
+  static_assert(EPI != 1 || (R == 2 && KSPLIT == 1), "the gate|up epilogue takes one row pair per wave");
   constexpr int kRowGroups = 4 / KSPLIT;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rg = wave / KSPLIT, ks = wave % KSPLIT;
   const int row0 = (blockIdx.x * kRowGroups + rg) * R;
   const int F = N >> 1, pj = blockIdx.x * kRowGroups + rg;       // EPI 1: pair index
-  auto row_of = [&](int r) { return EPI ? min(pj, F - 1) + r * F : min(row0 + r, N - 1); };
+  auto row_of = [&](int r) { return EPI == 1 ? min(pj, F - 1) + r * F : min(row0 + r, N - 1); };
   const int cpr = K >> 5;
   const int slice = (cpr + KSPLIT - 1) / KSPLIT;
   const int c_begin = ks * slice;
@@ -122,7 +140,8 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 #pragma unroll
       for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
       const int row = row0 + lane;
-      if (row < N) y[row] = v * tensor_scale[segment_of(segs, row)];
+      if (row < N) y[row] = EPI == 2 ? finish_row(v, tensor_scale[segment_of(segs, row)], row, lr)
+                                     : v * tensor_scale[segment_of(segs, row)];
     }
   } else {
     __shared__ float part[4][R];
@@ -136,7 +155,8 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 #pragma unroll
       for (int s = 0; s < KSPLIT; ++s) v += part[wave + s][lane];
       const int row = row0 + lane;
-      if (row < N) y[row] = v * tensor_scale[segment_of(segs, row)];
+      if (row < N) y[row] = EPI == 2 ? finish_row(v, tensor_scale[segment_of(segs, row)], row, lr)
+                                     : v * tensor_scale[segment_of(segs, row)];
     }
   }
 }
@@ -153,10 +173,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
                                                                    const float* __restrict__ tensor_scale, SegTable segs,
                                                                    const uint16_t* __restrict__ x, float* __restrict__ y,
                                                                    int N, int K, uint16_t* __restrict__ h = nullptr,
-                                                                   int act = 0) {
+                                                                   int act = 0, LowRank lr = {}) {
   static_assert(WAVES % KSPLIT == 0, "K split must divide the waves of a workgroup");
   static_assert(!XFIRST || XL, "x-first staging is an LDS staging");
-  static_assert(EPI == 0 || (R == 2 && KSPLIT == 1), "the gate|up epilogue takes one row pair per wave");
+  static_assert(EPI != 1 || (R == 2 && KSPLIT == 1), "the gate|up epilogue takes one row pair per wave");
   extern __shared__ u32x4 xs[];
   constexpr int kRowGroups = WAVES / KSPLIT;
   const int lane = threadIdx.x & 63;
@@ -164,7 +184,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   const int rg = wave / KSPLIT, ks = wave % KSPLIT;
   const int row0 = (blockIdx.x * kRowGroups + rg) * R;
   const int F = N >> 1, pj = blockIdx.x * kRowGroups + rg;       // EPI 1: pair index
-  auto row_of = [&](int r) { return EPI ? min(pj, F - 1) + r * F : min(row0 + r, N - 1); };
+  auto row_of = [&](int r) { return EPI == 1 ? min(pj, F - 1) + r * F : min(row0 + r, N - 1); };
   const int cpr = K >> 5;
   const int slice = (cpr + KSPLIT - 1) / KSPLIT;
   const int c_begin = ks * slice;
@@ -231,7 +251,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
 #pragma unroll
       for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
       const int row = row0 + lane;
-      if (row < N) y[row] = v * tensor_scale[segment_of(segs, row)];
+      if (row < N) y[row] = EPI == 2 ? finish_row(v, tensor_scale[segment_of(segs, row)], row, lr)
+                                     : v * tensor_scale[segment_of(segs, row)];
     }
   } else {
     __shared__ float part[WAVES][R];
@@ -245,7 +266,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
 #pragma unroll
       for (int k2 = 0; k2 < KSPLIT; ++k2) v += part[wave + k2][lane];
       const int row = row0 + lane;
-      if (row < N) y[row] = v * tensor_scale[segment_of(segs, row)];
+      if (row < N) y[row] = EPI == 2 ? finish_row(v, tensor_scale[segment_of(segs, row)], row, lr)
+                                     : v * tensor_scale[segment_of(segs, row)];
     }
   }
 }
@@ -290,6 +312,26 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
   }
 }
 
+// t[k] = sum_j x[j] V[j][k] (V [K][r] bf16, r <= 64) in one workgroup: thread (g, k) sums
+// j = g, g + G, ... (G = 1024 / r groups, consecutive threads read consecutive V entries), then
+// thread k adds the G partials in order, so the result does not depend on timing.
+__global__ __launch_bounds__(1024) void k_lowrank_t(const uint16_t* __restrict__ V, const uint16_t* __restrict__ x,
+                                                   float* __restrict__ t, int K, int r) {
+  __shared__ float part[1024];
+  const int G = 1024 / r;
+  const int tid = threadIdx.x, k = tid % r, g = tid / r;
+  float a = 0.0f;
+  if (g < G)
+    for (int j = g; j < K; j += G) a = __builtin_fmaf(bf16_bits_to_f32(x[j]), bf16_bits_to_f32(V[(size_t)j * r + k]), a);
+  part[tid] = a;
+  __syncthreads();
+  if (tid < r) {
+    float s = 0.0f;
+    for (int q = 0; q < G; ++q) s += part[q * r + tid];
+    t[tid] = s;
+  }
+}
+
 SegTable seg_table(const attnq_nvfp4& W) {
   SegTable t;
   t.n_seg = W.n_seg;
@@ -317,6 +359,23 @@ void launch_nvfp4_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, hip
   const size_t lds = XL ? (size_t)W.K * 2 : 0;
   k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI><<<grid, 64 * WAVES, lds, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
+}
+
+template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1>
+void launch_lr_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, const LowRank& lr, hipStream_t stream) {
+  constexpr int rows_per_wg = R * (WAVES / KSPLIT);
+  const unsigned grid = (unsigned)((W.N + rows_per_wg - 1) / rows_per_wg);
+  const size_t lds = XL ? (size_t)W.K * 2 : 0;
+  k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI, 2><<<grid, 64 * WAVES, lds, stream>>>(
+      W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K, nullptr, 0, lr);
+}
+
+template <int R, int KSPLIT>
+void launch_lr_loop(const attnq_nvfp4& W, const uint16_t* x, float* y, const LowRank& lr, hipStream_t stream) {
+  constexpr int rows_per_wg = R * (4 / KSPLIT);
+  const unsigned grid = (unsigned)((W.N + rows_per_wg - 1) / rows_per_wg);
+  k_gemv_nvfp4<R, KSPLIT, 2><<<grid, 256, 0, stream>>>(W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K,
+                                                       nullptr, 0, lr);
 }
 
 // gate|up epilogue launches: one row pair per wave, F = N / 2 pairs
@@ -347,6 +406,27 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
     launch_nvfp4_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 2 x 512 >= K/8)
   else
     launch_nvfp4_loop<2, 2>(W, x, y, stream);
+  return hipGetLastError();
+}
+
+// Runtime low-rank product over a shared NVFP4 block: t = V^T x (one workgroup), then the
+// streaming GEMV with the s / U t epilogue, in the same launch configurations as the plain GEMV.
+hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, const uint16_t* U, const uint16_t* V,
+                                     int r, const uint16_t* x, float* t, float* y, hipStream_t stream) {
+  if (W.N == 0) return hipSuccess;
+  if (r > 0) k_lowrank_t<<<1, 1024, 0, stream>>>(V, x, t, W.K, r);
+  const LowRank lr{s, U, t, r};
+  const int cpr = W.K / 32;
+  if (W.K >= 16384)
+    launch_lr_loop<4, 4>(W, x, y, lr, stream);
+  else if (cpr <= 128)
+    launch_lr_oneshot<2, 1, 2, true, 4, true, 2>(W, x, y, lr, stream);
+  else if (cpr <= 192 && W.N >= 16384)
+    launch_lr_oneshot<2, 1, 3, true, 8>(W, x, y, lr, stream);
+  else if (cpr <= 192)
+    launch_lr_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
+  else
+    launch_lr_loop<2, 2>(W, x, y, lr, stream);
   return hipGetLastError();
 }
 

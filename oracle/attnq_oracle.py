@@ -393,3 +393,36 @@ def gemv_nvfp4_glu(codes, scales, ts, x_bf16, rows=None) -> np.ndarray:
     g = gemv_nvfp4(codes, scales, ts, x_bf16, seg_end, rows=j)
     u = gemv_nvfp4(codes, scales, ts, x_bf16, seg_end, rows=j + F)
     return g, u
+
+
+# ---------------------------------------------------------------------------
+# runtime low-rank product over a shared NVFP4 block
+# ---------------------------------------------------------------------------
+def gemv_nvfp4_lowrank(codes, scales, ts, s_bf16, U_bf16, V_bf16, x_bf16, seg_end=None, rows=None) -> np.ndarray:
+    """y = s * (x . deq(W0)^T) + U (V^T x) in float64, never rebuilding the weight ("Throughput",
+    the runtime reconstruction path; weightless "Custom-op kernel" and "Trained weight sharing").
+    s is bf16 bits [N] or None (s = 1); U [N, r], V [K, r] bf16 bits or None (r = 0)."""
+    N = np.asarray(codes).shape[0]
+    idx = np.arange(N) if rows is None else np.asarray(rows)
+    y = gemv_nvfp4(codes, scales, ts, x_bf16, seg_end, rows=idx)
+    if s_bf16 is not None:
+        y = y * bf16_to_f32(np.asarray(s_bf16)[idx]).astype(np.float64)
+    if U_bf16 is not None and np.asarray(U_bf16).shape[1] > 0:
+        x = bf16_to_f32(x_bf16).astype(np.float64).reshape(-1)
+        t = bf16_to_f32(V_bf16).astype(np.float64).T @ x
+        y = y + bf16_to_f32(np.asarray(U_bf16)[idx]).astype(np.float64) @ t
+    return y
+
+
+def abs_lowrank(s_bf16, U_bf16, V_bf16, x_bf16, absdot_w0, rows=None) -> np.ndarray:
+    """|s| * sum_k |x_k w0_k| + sum_j |U_j| (sum_k |x_k V_kj|): the magnitude scale of the fp32
+    rounding error of the low-rank product, for any summation order."""
+    idx = slice(None) if rows is None else np.asarray(rows)
+    out = np.asarray(absdot_w0, dtype=np.float64).copy()
+    if s_bf16 is not None:
+        out = out * np.abs(bf16_to_f32(np.asarray(s_bf16)[idx]).astype(np.float64))
+    if U_bf16 is not None and np.asarray(U_bf16).shape[1] > 0:
+        x = np.abs(bf16_to_f32(x_bf16).astype(np.float64)).reshape(-1)
+        t = np.abs(bf16_to_f32(V_bf16).astype(np.float64)).T @ x
+        out = out + np.abs(bf16_to_f32(np.asarray(U_bf16)[idx]).astype(np.float64)) @ t
+    return out

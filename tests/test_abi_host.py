@@ -25,10 +25,11 @@ def _declared_functions():
     return sorted(set(re.findall(r"ATTNQ_API\s+[\w\s\*]+?\b(attnq_\w+)\s*\(", text)))
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_every_call():
     names = _declared_functions()
     for n in ["attnq_reconstruct", "attnq_quantize_nvfp4", "attnq_gemv_nvfp4", "attnq_gemv_bf16",
-              "attnq_gemm_nvfp4_small_m", "attnq_status_string"]:
+              "attnq_gemm_nvfp4_small_m", "attnq_gemv_nvfp4_glu", "attnq_gemv_nvfp4_lowrank",
+              "attnq_status_string"]:
         assert n in names
 
 
@@ -141,6 +142,20 @@ def test_gemv_and_gemm_validation():
     assert glu(ctypes.byref(pair), FAKE, 0, None, None) == 1
     assert glu(ctypes.byref(pair), FAKE + 8, 0, FAKE, None) == 3
     assert glu(ctypes.byref(pair), FAKE, 1, FAKE + 1, None) == 3                  # h needs 2-byte alignment
+    lr = lib.attnq_gemv_nvfp4_lowrank
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE, 65, FAKE, FAKE, FAKE, None) == 2       # r > 64
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, None) == 2
+    assert lr(ctypes.byref(nv), FAKE, None, FAKE, 4, FAKE, FAKE, FAKE, None) == 1        # U missing
+    assert lr(ctypes.byref(nv), FAKE, FAKE, None, 4, FAKE, FAKE, FAKE, None) == 1        # V missing
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, None) == 1        # t missing
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE, 4, None, FAKE, FAKE, None) == 1        # x missing
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, None) == 1        # y missing
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE, 4, FAKE + 8, FAKE, FAKE, None) == 3    # x 16-byte
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE, 4, FAKE, FAKE + 2, FAKE, None) == 3    # t 4-byte
+    assert lr(ctypes.byref(nv), FAKE + 1, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 3    # s 2-byte
+    assert lr(ctypes.byref(nv), FAKE, FAKE + 1, FAKE, 4, FAKE, FAKE, FAKE, None) == 3    # U 2-byte
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE + 1, 4, FAKE, FAKE, FAKE, None) == 3    # V 2-byte
+    assert lr(ctypes.byref(_nv(K=16)), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 2
     g = lib.attnq_gemm_nvfp4_small_m
     assert g(ctypes.byref(nv), FAKE, 17, 64, FAKE, 64, None) == 2                 # M > 16
     assert g(ctypes.byref(nv), FAKE, 4, 32, FAKE, 64, None) == 2                  # ldx < K

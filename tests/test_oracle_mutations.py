@@ -102,3 +102,40 @@ def test_dropped_block_is_caught(monkeypatch):
         return out
     monkeypatch.setattr(OM, "unpack_codes", drop_last_block)
     assert _fails(PG.test_gemv_equals_exact_rational_sum)
+
+
+def _lowrank_mutant(monkeypatch, slip):
+    """Replace the oracle's low-rank product by a version with one slip written in."""
+    def mutated(codes, scales, ts, s_bf16, U_bf16, V_bf16, x_bf16, seg_end=None, rows=None):
+        y = OM.gemv_nvfp4(codes, scales, ts, x_bf16, seg_end)
+        sv = OM.bf16_to_f32(np.asarray(s_bf16)).astype(np.float64)
+        x = OM.bf16_to_f32(x_bf16).astype(np.float64).reshape(-1)
+        U = OM.bf16_to_f32(np.asarray(U_bf16)).astype(np.float64)
+        V = OM.bf16_to_f32(np.asarray(V_bf16)).astype(np.float64)
+        return slip(y, sv, x, U, V)
+    monkeypatch.setattr(OM, "gemv_nvfp4_lowrank", mutated)
+    monkeypatch.setattr(O, "gemv_nvfp4_lowrank", mutated)
+
+
+def test_lowrank_scale_on_the_delta_is_caught(monkeypatch):
+    import test_oracle_lowrank as PL
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V: s * (y + U @ (V.T @ x)))
+    assert _fails(PL.test_lowrank_equals_exact_rational_sum)
+
+
+def test_lowrank_reversed_factor_rows_are_caught(monkeypatch):
+    import test_oracle_lowrank as PL
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V: s * y + U @ (V[::-1].T @ x))
+    assert _fails(PL.test_lowrank_equals_exact_rational_sum)
+
+
+def test_lowrank_delta_sign_slip_is_caught(monkeypatch):
+    import test_oracle_lowrank as PL
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V: s * y - U @ (V.T @ x))
+    assert _fails(PL.test_lowrank_equals_exact_rational_sum)
+
+
+def test_lowrank_dropped_rank_is_caught(monkeypatch):
+    import test_oracle_lowrank as PL
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V: s * y + U[:, :-1] @ (V[:, :-1].T @ x))
+    assert _fails(PL.test_lowrank_equals_exact_rational_sum)
