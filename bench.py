@@ -12,10 +12,13 @@ own workload -- all 410 theta bundles at rank 16 with s ~ U(0.9, 1.1) (420 segme
 quantizations: in 10 layers k's bundle also fills the v rows) -- and so is the small-M verify
 product (M = 4 and 8) on one layer; both are reported as extra fields.
 
-Two more token streams are timed the same way and reported under "streams": the chained token
+Three more token streams are timed the same way and reported under "streams": the chained token
 in which each layer's gate|up launch applies the activation epilogue (attnq_gemv_nvfp4_glu)
-and its down projection reads that bf16 output, and the coverage-matched mix with the attention
-projections left in bf16 (attnq_gemv_bf16) and the MLP in NVFP4.
+and its down projection reads that bf16 output; the coverage-matched mix with the attention
+projections left in bf16 (attnq_gemv_bf16) and the MLP in NVFP4; and the runtime low-rank token,
+26 shared NVFP4 blocks in contiguous bands of layers, each layer applying its own rank-16
+s, U, V in the GEMV epilogue (attnq_gemv_nvfp4_lowrank). Consecutive layers of one band read the
+same block, so part of that stream's block bytes may come from the last-level cache.
 
 Output: one JSON line (see the design doc for the fields). Options:
   --steps K --warmup W       timed / untimed steps (defaults 20 / 5)
@@ -49,6 +52,8 @@ VOCAB = 262144
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 VALU_FP32_PEAK_TFLOPS = 157.3  # published fp32 vector peak (packed), for the load path note
 PROJ_NAMES = ("qkv", "o", "gate_up", "down")
+LOWRANK_BANDS = 26             # shared NVFP4 blocks for the 60 layers, in contiguous bands
+LOWRANK_RANK = 16
 
 # HBM traffic of one fused gate|up launch from the FETCH_SIZE / WRITE_SIZE passes recorded in
 # profiles/gemv_nvfp4_31b_token_traffic.md (FETCH scaled x1.9999, WRITE x1.0 by a 1 GiB copy).
@@ -102,6 +107,7 @@ class Model:
         # gate|up activation output per layer (the input of down in the chained stream)
         self.h = [torch.empty(GU_SEGS[0], dtype=torch.bfloat16, device=dev) for _ in range(N_LAYERS)]
         self.attn_bf16 = None
+        self.lowrank = None
 
     def quantize_passthrough(self, dev):
         """Fill every NVFP4 weight from a seeded device bf16 W0 (passthrough reconstruction)."""
@@ -158,6 +164,57 @@ class Model:
                 W, x, y, _, _ = lay[name]
                 A.attnq_gemv_nvfp4(W, x, y)
         A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
+
+    def build_lowrank(self, dev):
+        """Runtime low-rank stream: 26 shared NVFP4 blocks (the first 26 layers' weights), layer L
+        reading block L * 26 // 60, each layer with its own per-segment s, U, V at rank 16."""
+        from nvfp4_weight_only_rtn_amd import inputs
+        r = LOWRANK_RANK
+        seed = 80_000
+        self.lowrank = []
+        for L in range(N_LAYERS):
+            band = L * LOWRANK_BANDS // N_LAYERS
+            lay = {}
+            for name in PROJ_NAMES:
+                W, _, _, segs, K = self.layers[band][name]
+                _, x, y, _, _ = self.layers[L][name]
+                s = inputs.device_uniform_bf16((W.N,), 0.9, 1.1, seed=seed, device=dev)
+                U = inputs.device_normal_bf16((W.N, r), 1e-3, seed=seed + 1, device=dev)
+                V = inputs.device_normal_bf16((len(segs), K, r), 1e-3, seed=seed + 2, device=dev)
+                t = torch.empty(self.A.attnq_gemv_nvfp4_lowrank_workspace(K, len(segs), r), dtype=torch.float32,
+                                device=dev)
+                seed += 3
+                lay[name] = (W, s, U, V, t, x, y)
+            self.lowrank.append(lay)
+
+    def lowrank_step(self):
+        """Every projection as shared NVFP4 block + its own low-rank delta, never rebuilt
+        (attnq_gemv_nvfp4_lowrank: the t = V^T x kernel, then the GEMV with the s / U t epilogue)."""
+        A = self.A
+        for lay in self.lowrank:
+            for name in PROJ_NAMES:
+                W, s, U, V, t, x, y = lay[name]
+                A.attnq_gemv_nvfp4_lowrank(W, s, U, V, x, t, y)
+        A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
+
+    def lowrank_bytes_per_step(self) -> int:
+        """Per launch: the block's NVFP4 bytes + x + y, plus s (2N), U (2Nr), V (2 n_seg K r), the
+        partial-sum kernel's x reads (2K per segment) and its partials written and read once (8 per value)."""
+        r = LOWRANK_RANK
+        total = 0
+        for lay in self.lowrank:
+            for name in PROJ_NAMES:
+                W, s, U, V, t, x, y = lay[name]
+                n_seg = len(W.seg_end)
+                total += nvfp4_bytes(W.N, W.K, n_seg) + 2 * W.N + 2 * W.N * r + 2 * n_seg * W.K * r + \
+                    2 * W.K * n_seg + 8 * t.numel()
+        return total + bf16_bytes(VOCAB, HIDDEN)
+
+    def lowrank_resident_bytes(self) -> int:
+        blocks = sum(self.layers[b][n][0].nbytes for b in range(LOWRANK_BANDS) for n in PROJ_NAMES)
+        factors = sum(lay[n][1].numel() * 2 + lay[n][2].numel() * 2 + lay[n][3].numel() * 2
+                      for lay in self.lowrank for n in PROJ_NAMES)
+        return blocks + factors + 2 * VOCAB * HIDDEN
 
     def glu_bytes_per_step(self) -> int:
         total = 0
@@ -448,6 +505,11 @@ def main():
     mixed_ms = graph_timing(model.mixed_step, args.warmup, args.steps)
     mixed_bytes = model.mixed_bytes_per_step()
     model.attn_bf16 = None
+    model.build_lowrank(dev)
+    lr_ms = graph_timing(model.lowrank_step, args.warmup, args.steps)
+    lr_bytes = model.lowrank_bytes_per_step()
+    lr_resident = model.lowrank_resident_bytes()
+    model.lowrank = None
     torch.cuda.empty_cache()
     streams = {
         "glu_chained": {"what": "gate|up GEMV with the gelu-tanh epilogue writing bf16 h, down reading h",
@@ -456,6 +518,12 @@ def main():
         "bf16_attention": {"what": "q|k|v and o in bf16 (attnq_gemv_bf16), gate|up and down NVFP4, bf16 lm_head",
                            "ms_per_token": round(mixed_ms, 5), "bytes_per_token": mixed_bytes,
                            "TBps": round(mixed_bytes / (mixed_ms * 1e-3) / 1e12, 4)},
+        "lowrank_banded": {"what": f"runtime low-rank: {LOWRANK_BANDS} shared NVFP4 blocks in contiguous bands of layers, "
+                                   f"per-layer per-segment s, U, V at rank {LOWRANK_RANK} applied in the GEMV epilogue "
+                                   "(attnq_gemv_nvfp4_lowrank, 2 launches per projection), bf16 lm_head",
+                           "ms_per_token": round(lr_ms, 5), "bytes_per_token": lr_bytes,
+                           "resident_weight_bytes": lr_resident,
+                           "TBps": round(lr_bytes / (lr_ms * 1e-3) / 1e12, 4)},
     }
     log(f"streams: {streams}")
 

@@ -151,22 +151,33 @@ ATTNQ_API attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x,
 ATTNQ_API attnq_status attnq_gemv_nvfp4_glu(const attnq_nvfp4* W, const uint16_t* x, int32_t act, uint16_t* h,
                                   attnq_stream stream);
 
-/* Runtime low-rank product over a shared NVFP4 block, the weight never rebuilt:
- *   y[n] = s[n] * (sum_k x[k] * weight0[n][k]) + sum_j U[n][j] * t[j],  t[j] = sum_k x[k] * V[k][j]
+/* Runtime low-rank product over a shared NVFP4 block, the weight never rebuilt: for a row n of
+ * segment g (each segment is one projection with its own factors, as in a fused q|k|v),
+ *   y[n] = s[n] * (sum_k x[k] * weight0[n][k]) + sum_j U[n][j] * t[g][j],  t[g][j] = sum_k x[k] * V[g][k][j]
  * ("Throughput", "The runtime reconstruction path does not reach dense parity": W0 and the
  * low-rank delta applied on every forward pass; weightless "GPU and cache acceleration",
  * "Architecture decisions / Custom-op kernel": the W0 dot product and the low-rank delta fused in
  * one kernel with nothing materialized; "Future work / Trained weight sharing": a shared NVFP4 W0
  * plus a bf16 low-rank pair). W0 is an NVFP4 weight [N][K] that several projections may share
- * (each call reads it once); s [N] bf16 or NULL (s = 1); U [N][r], V [K][r] bf16 row-major,
- * NULL when r == 0 (U may also be NULL when N == 0), 0 <= r <= 64. t is a caller-owned fp32 workspace of r values that receives
- * V^T x (NULL iff r == 0). Two kernels in stream order: t (one workgroup, fixed summation order),
- * then the streaming GEMV whose epilogue applies s and U t. fp32 arithmetic throughout.
- * x 16-byte aligned, y and t 4-byte aligned, s / U / V 2-byte aligned; y must not overlap the
- * inputs. Errors: as attnq_gemv_nvfp4; r outside [0, 64] is ATTNQ_ERR_SHAPE. */
+ * (each call reads it once); s [N] bf16 or NULL (s = 1); U [N][r] and V [n_seg][K][r] bf16
+ * row-major, NULL when r == 0 (U may also be NULL when N == 0), 0 <= r <= 64.
+ * ws is a caller-owned fp32 workspace of at least attnq_gemv_nvfp4_lowrank_workspace(K, n_seg, r)
+ * values (NULL when r == 0); it receives partial sums of V[g]^T x, P per segment, each over
+ * floor(8192 / r) consecutive k: ws[(g * P + p) * r + j], P = ceil(K / floor(8192 / r)).
+ * Two kernels in stream order: the partial sums, then the streaming GEMV, which reduces them to
+ * t and applies s and U t in its epilogue. fp32 arithmetic; every sum is taken in a fixed order,
+ * so repeated calls give identical bits. x and V 16-byte aligned, y and ws 4-byte aligned, s and
+ * U 2-byte aligned; y and ws must not overlap the inputs or each other. Calls that share one ws
+ * must be ordered on one stream. Errors: as attnq_gemv_nvfp4; r outside [0, 64] is
+ * ATTNQ_ERR_SHAPE. */
 ATTNQ_API attnq_status attnq_gemv_nvfp4_lowrank(const attnq_nvfp4* W0, const uint16_t* s, const uint16_t* U,
-                                      const uint16_t* V, int32_t r, const uint16_t* x, float* t, float* y,
+                                      const uint16_t* V, int32_t r, const uint16_t* x, float* ws, float* y,
                                       attnq_stream stream);
+
+/* Number of fp32 values the workspace of attnq_gemv_nvfp4_lowrank needs for a weight of row length
+ * K with n_seg segments at rank r (0 when r == 0), or -1 if K, n_seg or r is out of range. Host
+ * only, no GPU call. */
+ATTNQ_API int64_t attnq_gemv_nvfp4_lowrank_workspace(int32_t K, int32_t n_seg, int32_t r);
 
 /* y[n] = sum_k x[k] * W[n][k] for a bf16 weight [N][K] (the tied lm_head, or projections
  * left in bf16). W and x 16-byte aligned, y 4-byte aligned. fp32 accumulation. */

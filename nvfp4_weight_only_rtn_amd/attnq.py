@@ -50,6 +50,8 @@ _SIGS = {
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
     getattr(_lib, _name).restype = _S
+_lib.attnq_gemv_nvfp4_lowrank_workspace.argtypes = [_I, _I, _I]
+_lib.attnq_gemv_nvfp4_lowrank_workspace.restype = ctypes.c_int64
 _lib.attnq_status_string.argtypes = [_S]
 _lib.attnq_status_string.restype = ctypes.c_char_p
 
@@ -135,10 +137,16 @@ def attnq_gemv_nvfp4_glu(W: NVFP4Weight, x, act: int, h, stream=None) -> None:
     _check(_lib.attnq_gemv_nvfp4_glu(ctypes.byref(W.desc()), _ptr(x, 2), act, _ptr(h, 2), _stream(stream)))
 
 
-def attnq_gemv_nvfp4_lowrank(W0: NVFP4Weight, s, U, V, x, t, y, stream=None) -> None:
+def attnq_gemv_nvfp4_lowrank_workspace(K: int, n_seg: int, r: int) -> int:
+    return int(_lib.attnq_gemv_nvfp4_lowrank_workspace(K, n_seg, r))
+
+
+def attnq_gemv_nvfp4_lowrank(W0: NVFP4Weight, s, U, V, x, ws, y, stream=None) -> None:
     r = 0 if U is None else U.shape[1]
+    if r and (ws is None or ws.numel() < attnq_gemv_nvfp4_lowrank_workspace(W0.K, len(W0.seg_end), r)):
+        raise ValueError("attnq_gemv_nvfp4_lowrank: workspace smaller than attnq_gemv_nvfp4_lowrank_workspace()")
     _check(_lib.attnq_gemv_nvfp4_lowrank(ctypes.byref(W0.desc()), _ptr(s, 2), _ptr(U, 2), _ptr(V, 2), r, _ptr(x, 2),
-                                         _ptr(t, 4), _ptr(y, 4), _stream(stream)))
+                                         _ptr(ws, 4), _ptr(y, 4), _stream(stream)))
 
 
 def attnq_gemv_bf16(W, x, y, stream=None) -> None:

@@ -67,21 +67,111 @@ __device__ __forceinline__ void store_glu(uint16_t* h, int j, float g, float u, 
   h[j] = (uint16_t)(__builtin_bit_cast(uint32_t, p) & 0xFFFFu);
 }
 
-// Runtime low-rank epilogue (EPI 2): y[row] = s[row] * (x . weight0[row]) + sum_k U[row][k] t[k],
-// with t = V^T x computed beforehand by k_lowrank_t.
+// Runtime low-rank epilogue (EPI 2): for a row of segment g,
+//   y[row] = s[row] * (x . weight0[row]) + sum_k U[row][k] t[g][k],  t[g] = V[g]^T x.
+// k_lowrank_part leaves P partial sums of t per segment (one per 16 KB chunk of V); each GEMV
+// workgroup loads its segment's partials right after issuing its weight loads, reduces them to
+// t in LDS after the main loop, and each wave adds U[row] . t across its lanes. Every sum is
+// taken in one fixed order, so the result does not depend on timing or on the launch shape.
+constexpr int kLrThreads = 256;     // threads of the partial-sum kernel and of the t reduction
+constexpr int kLrChunk = 8192;      // V elements behind one partial (16 KB of bf16)
+constexpr int kLrPrefetch = 4;      // partials per thread loaded ahead of the main loop
+
 struct LowRank {
-  const uint16_t* s;   // [N] bf16 or null (s = 1)
-  const uint16_t* U;   // [N][r] bf16
-  const float* t;      // [r] fp32
-  int r;
+  const uint16_t* s;     // [N] bf16 or null (s = 1)
+  const uint16_t* U;     // [N][r] bf16
+  const float* part;     // [n_seg][P][r] partial sums of V^T x
+  int r, P;
 };
 
-__device__ __forceinline__ float finish_row(float v, float ts, int row, const LowRank& lr) {
+// t[g][k] in the kernels' order: sum over q < Q of (sum over p = q, q + Q, ... of part[g][p][k]),
+// Q = 256 / r. Used for the rare workgroup whose rows reach into a second segment.
+__device__ __forceinline__ float lr_t_direct(const LowRank& lr, int g, int k) {
+  const int Q = kLrThreads / lr.r;
+  const float* pg = lr.part + (size_t)g * lr.P * lr.r;
+  float t = 0.0f;
+  for (int q = 0; q < Q; ++q) {
+    float a = 0.0f;
+    for (int p = q; p < lr.P; p += Q) a += pg[(size_t)p * lr.r + k];
+    t += a;
+  }
+  return t;
+}
+
+template <int R>
+struct LrRegs {
+  float pv[kLrPrefetch];   // this thread's partials of segment g0
+  float uv[R];             // U[row][lane] of the wave's rows (lane < r)
+  float sv;                // s of the row this lane stores (lane < R)
+  int g0;                  // segment of the workgroup's first row
+};
+
+// Thread (q, k) = (tid / r, tid % r) of the first 256 loads part[g0][p][k] for p = q, q + Q, ...
+template <int R, class RowOf>
+__device__ __forceinline__ void lr_prefetch(LrRegs<R>& st, const LowRank& lr, const SegTable& segs, int wg_first,
+                                            const RowOf& row_of, int lane) {
+  st.g0 = segment_of(segs, wg_first);
+  st.sv = (lr.s != nullptr && lane < R) ? bf16_bits_to_f32(lr.s[row_of(lane)]) : 1.0f;
+#pragma unroll
+  for (int u = 0; u < kLrPrefetch; ++u) st.pv[u] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) st.uv[r] = 0.0f;
+  if (lr.r == 0) return;
+  const int tid = threadIdx.x, Q = kLrThreads / lr.r, q = tid / lr.r, k = tid - q * lr.r;
+  const float* pg = lr.part + (size_t)st.g0 * lr.P * lr.r;
+  if (tid < kLrThreads && q < Q) {
+#pragma unroll
+    for (int u = 0; u < kLrPrefetch; ++u)
+      if (q + u * Q < lr.P) st.pv[u] = pg[(size_t)(q + u * Q) * lr.r + k];
+  }
+  if (lane < lr.r) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) st.uv[r] = bf16_bits_to_f32(lr.U[(size_t)row_of(r) * lr.r + lane]);
+  }
+}
+
+// All threads of the workgroup: t of the segments g0 .. segment(wg_last) into tl[g - g0][k].
+template <int R>
+__device__ __forceinline__ void lr_reduce(const LrRegs<R>& st, const LowRank& lr, const SegTable& segs, int wg_last,
+                                          float* l1, float* tl) {
+  if (lr.r == 0) return;
+  const int tid = threadIdx.x, Q = kLrThreads / lr.r, q = tid / lr.r, k = tid - q * lr.r;
+  if (tid < kLrThreads) {
+    float a = 0.0f;
+    if (q < Q) {
+#pragma unroll
+      for (int u = 0; u < kLrPrefetch; ++u) a += st.pv[u];
+      const float* pg = lr.part + (size_t)st.g0 * lr.P * lr.r;
+      for (int p = q + kLrPrefetch * Q; p < lr.P; p += Q) a += pg[(size_t)p * lr.r + k];
+    }
+    l1[tid] = a;
+  }
+  __syncthreads();
+  if (tid < lr.r) {
+    float t = 0.0f;
+    for (int qq = 0; qq < Q; ++qq) t += l1[qq * lr.r + tid];
+    tl[tid] = t;
+    const int g_last = segment_of(segs, wg_last);
+    for (int g = st.g0 + 1; g <= g_last; ++g) tl[(g - st.g0) * 64 + tid] = lr_t_direct(lr, g, tid);
+  }
+  __syncthreads();
+}
+
+// d[r] = U[row_r] . t[segment of row_r], summed across the wave (every lane gets the sums).
+template <int R, class RowOf>
+__device__ __forceinline__ void lr_row_terms(const LrRegs<R>& st, const LowRank& lr, const SegTable& segs,
+                                             const float* tl, const RowOf& row_of, int lane, float* d) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float c = 0.0f;
+    if (lane < lr.r) c = st.uv[r] * tl[(segment_of(segs, row_of(r)) - st.g0) * 64 + lane];
+    d[r] = wave_sum(c);
+  }
+}
+
+__device__ __forceinline__ float lr_finish(float v, float ts, float s, float d) {
   v *= ts;
-  if (lr.s) v *= bf16_bits_to_f32(lr.s[row]);
-  float d = 0.0f;
-  const uint16_t* u = lr.U + (size_t)row * lr.r;
-  for (int k = 0; k < lr.r; ++k) d = __builtin_fmaf(bf16_bits_to_f32(u[k]), lr.t[k], d);
+  v *= s;
   return v + d;
 }
 
@@ -111,6 +201,9 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  [[maybe_unused]] LrRegs<R> lrs;
+  [[maybe_unused]] const int wg_first = blockIdx.x * kRowGroups * R;
+  if constexpr (EPI == 2) lr_prefetch<R>(lrs, lr, segs, wg_first, row_of, lane);
 
   for (int c = c_begin + lane; c < c_end; c += 64) {
     const u32x4* xp = reinterpret_cast<const u32x4*>(x + (size_t)c * kChunkElems);
@@ -131,6 +224,17 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  [[maybe_unused]] float lrd = 0.0f;
+  if constexpr (EPI == 2) {
+    __shared__ float lr_l1[kLrThreads];
+    __shared__ float lr_t[ATTNQ_MAX_SEGMENTS * 64];
+    lr_reduce<R>(lrs, lr, segs, min(N, wg_first + kRowGroups * R) - 1, lr_l1, lr_t);
+    float d[R];
+    lr_row_terms<R>(lrs, lr, segs, lr_t, row_of, lane, d);
+    lrd = d[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) lrd = (lane == r) ? d[r] : lrd;
+  }
 
   if constexpr (EPI == 1) {
     if (lane == 0 && pj < F) store_glu(h, pj, acc[0] * tensor_scale[0], acc[1] * tensor_scale[1], act);
@@ -140,7 +244,7 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 #pragma unroll
       for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
       const int row = row0 + lane;
-      if (row < N) y[row] = EPI == 2 ? finish_row(v, tensor_scale[segment_of(segs, row)], row, lr)
+      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lrs.sv, lrd)
                                      : v * tensor_scale[segment_of(segs, row)];
     }
   } else {
@@ -155,7 +259,7 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 #pragma unroll
       for (int s = 0; s < KSPLIT; ++s) v += part[wave + s][lane];
       const int row = row0 + lane;
-      if (row < N) y[row] = EPI == 2 ? finish_row(v, tensor_scale[segment_of(segs, row)], row, lr)
+      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lrs.sv, lrd)
                                      : v * tensor_scale[segment_of(segs, row)];
     }
   }
@@ -210,6 +314,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
       sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
     }
   }
+  [[maybe_unused]] LrRegs<R> lrs;
+  [[maybe_unused]] const int wg_first = blockIdx.x * kRowGroups * R;
+  if constexpr (EPI == 2) lr_prefetch<R>(lrs, lr, segs, wg_first, row_of, lane);
   if constexpr (XFIRST) {
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
@@ -243,6 +350,17 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  [[maybe_unused]] float lrd = 0.0f;
+  if constexpr (EPI == 2) {
+    __shared__ float lr_l1[kLrThreads];
+    __shared__ float lr_t[ATTNQ_MAX_SEGMENTS * 64];
+    lr_reduce<R>(lrs, lr, segs, min(N, wg_first + kRowGroups * R) - 1, lr_l1, lr_t);
+    float d[R];
+    lr_row_terms<R>(lrs, lr, segs, lr_t, row_of, lane, d);
+    lrd = d[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) lrd = (lane == r) ? d[r] : lrd;
+  }
   if constexpr (EPI == 1) {
     if (lane == 0 && pj < F) store_glu(h, pj, acc[0] * tensor_scale[0], acc[1] * tensor_scale[1], act);
   } else if constexpr (KSPLIT == 1) {
@@ -251,7 +369,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
 #pragma unroll
       for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
       const int row = row0 + lane;
-      if (row < N) y[row] = EPI == 2 ? finish_row(v, tensor_scale[segment_of(segs, row)], row, lr)
+      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lrs.sv, lrd)
                                      : v * tensor_scale[segment_of(segs, row)];
     }
   } else {
@@ -266,7 +384,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
 #pragma unroll
       for (int k2 = 0; k2 < KSPLIT; ++k2) v += part[wave + k2][lane];
       const int row = row0 + lane;
-      if (row < N) y[row] = EPI == 2 ? finish_row(v, tensor_scale[segment_of(segs, row)], row, lr)
+      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lrs.sv, lrd)
                                      : v * tensor_scale[segment_of(segs, row)];
     }
   }
@@ -312,23 +430,71 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
   }
 }
 
-// t[k] = sum_j x[j] V[j][k] (V [K][r] bf16, r <= 64) in one workgroup: thread (g, k) sums
-// j = g, g + G, ... (G = 1024 / r groups, consecutive threads read consecutive V entries), then
-// thread k adds the G partials in order, so the result does not depend on timing.
-__global__ __launch_bounds__(1024) void k_lowrank_t(const uint16_t* __restrict__ V, const uint16_t* __restrict__ x,
-                                                   float* __restrict__ t, int K, int r) {
-  __shared__ float part[1024];
-  const int G = 1024 / r;
-  const int tid = threadIdx.x, k = tid % r, g = tid / r;
-  float a = 0.0f;
-  if (g < G)
-    for (int j = g; j < K; j += G) a = __builtin_fmaf(bf16_bits_to_f32(x[j]), bf16_bits_to_f32(V[(size_t)j * r + k]), a);
-  part[tid] = a;
+// part[g][p][k] = sum over the rows j of chunk p of x[j] V[g][j][k] (V [n_seg][K][r] bf16), one
+// workgroup per (chunk, segment); a chunk is floor(8192 / r) rows of V. For r a power of two a
+// thread loads four 16-byte pieces of the chunk, and its element i always falls in column
+// (8 tid + i) mod r, so it keeps eight column sums; the workgroup then adds slots of one column
+// in a fixed tree. Other ranks take one column per thread and 2-byte loads.
+__global__ __launch_bounds__(kLrThreads) void k_lowrank_part(const uint16_t* __restrict__ V,
+                                                             const uint16_t* __restrict__ x, float* __restrict__ part,
+                                                             int K, int r, int P) {
+  __shared__ float l1[kLrThreads * 8];
+  __shared__ uint16_t xl[kLrChunk];
+  const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int KC = kLrChunk / r, j0 = p * KC, rows = min(KC, K - j0);
+  const uint16_t* Vc = V + ((size_t)g * K + j0) * r;
+  for (int j = tid; j < rows; j += kLrThreads) xl[j] = x[j0 + j];
   __syncthreads();
-  if (tid < r) {
-    float s = 0.0f;
-    for (int q = 0; q < G; ++q) s += part[q * r + tid];
-    t[tid] = s;
+  float* out = part + ((size_t)g * P + p) * r;
+  if ((r & (r - 1)) == 0) {
+    const int sh = __builtin_ctz(r), E = rows * r;          // E is a multiple of 32
+    u32x4 v[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e0 = (m * kLrThreads + tid) * 8;
+      v[m] = e0 < E ? *reinterpret_cast<const u32x4*>(Vc + e0) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e0 = (m * kLrThreads + tid) * 8;
+      if (e0 < E) {
+        const uint32_t w[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float vi = __builtin_bit_cast(float, (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+          acc[i] = __builtin_fmaf(bf16_bits_to_f32(xl[(e0 + i) >> sh]), vi, acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l1[tid * 8 + i] = acc[i];
+    __syncthreads();
+    float a = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += l1[tid + u * kLrThreads];   // slots of column tid mod r
+    __syncthreads();
+    l1[tid] = a;
+    __syncthreads();
+    if (tid < r) {
+      float t = 0.0f;
+      for (int q = 0; q < kLrThreads / r; ++q) t += l1[q * r + tid];
+      out[tid] = t;
+    }
+  } else {
+    const int G = kLrThreads / r, q = tid / r, k = tid - q * r;
+    float a = 0.0f;
+    if (q < G)
+      for (int j = q; j < rows; j += G) a = __builtin_fmaf(bf16_bits_to_f32(xl[j]), bf16_bits_to_f32(Vc[(size_t)j * r + k]), a);
+    l1[tid] = a;
+    __syncthreads();
+    if (tid < r) {
+      float t = 0.0f;
+      for (int qq = 0; qq < G; ++qq) t += l1[qq * r + tid];
+      out[tid] = t;
+    }
   }
 }
 
@@ -359,6 +525,11 @@ void launch_nvfp4_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, hip
   const size_t lds = XL ? (size_t)W.K * 2 : 0;
   k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI><<<grid, 64 * WAVES, lds, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
+}
+
+int lowrank_parts(int K, int r) {
+  const int KC = kLrChunk / r;
+  return (K + KC - 1) / KC;
 }
 
 template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1>
@@ -409,13 +580,21 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
   return hipGetLastError();
 }
 
-// Runtime low-rank product over a shared NVFP4 block: t = V^T x (one workgroup), then the
-// streaming GEMV with the s / U t epilogue, in the same launch configurations as the plain GEMV.
+// Runtime low-rank product over a shared NVFP4 block: the partial sums of t = V^T x (one
+// workgroup per 16 KB chunk of V and segment), then the streaming GEMV with the s / U t epilogue,
+// in the same launch configurations as the plain GEMV.
+int64_t lowrank_workspace_floats(int K, int n_seg, int r) {
+  return r == 0 ? 0 : (int64_t)n_seg * lowrank_parts(K, r) * r;
+}
+
 hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, const uint16_t* U, const uint16_t* V,
-                                     int r, const uint16_t* x, float* t, float* y, hipStream_t stream) {
+                                     int r, const uint16_t* x, float* ws, float* y, hipStream_t stream) {
   if (W.N == 0) return hipSuccess;
-  if (r > 0) k_lowrank_t<<<1, 1024, 0, stream>>>(V, x, t, W.K, r);
-  const LowRank lr{s, U, t, r};
+  LowRank lr{s, U, ws, r, 0};
+  if (r > 0) {
+    lr.P = lowrank_parts(W.K, r);
+    k_lowrank_part<<<dim3((unsigned)lr.P, (unsigned)W.n_seg), kLrThreads, 0, stream>>>(V, x, ws, W.K, r, lr.P);
+  }
   const int cpr = W.K / 32;
   if (W.K >= 16384)
     launch_lr_loop<4, 4>(W, x, y, lr, stream);

@@ -14,7 +14,8 @@ hipError_t launch_quantize(const attnq_theta& theta, uint8_t* codes, uint8_t* sc
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_gemv_nvfp4_glu(const attnq_nvfp4& W, const uint16_t* x, int act, uint16_t* h, hipStream_t stream);
 hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, const uint16_t* U, const uint16_t* V,
-                                     int r, const uint16_t* x, float* t, float* y, hipStream_t stream);
+                                     int r, const uint16_t* x, float* ws, float* y, hipStream_t stream);
+int64_t lowrank_workspace_floats(int K, int n_seg, int r);
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_gemm_nvfp4_small_m(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
                                      hipStream_t stream);

@@ -399,9 +399,11 @@ def gemv_nvfp4_glu(codes, scales, ts, x_bf16, rows=None) -> np.ndarray:
 # runtime low-rank product over a shared NVFP4 block
 # ---------------------------------------------------------------------------
 def gemv_nvfp4_lowrank(codes, scales, ts, s_bf16, U_bf16, V_bf16, x_bf16, seg_end=None, rows=None) -> np.ndarray:
-    """y = s * (x . deq(W0)^T) + U (V^T x) in float64, never rebuilding the weight ("Throughput",
-    the runtime reconstruction path; weightless "Custom-op kernel" and "Trained weight sharing").
-    s is bf16 bits [N] or None (s = 1); U [N, r], V [K, r] bf16 bits or None (r = 0)."""
+    """y = s * (x . deq(W0)^T) + U (V_g^T x) in float64 for a row of segment g, never rebuilding the
+    weight ("Throughput", the runtime reconstruction path; weightless "Custom-op kernel" and
+    "Trained weight sharing"). Each segment is one projection with its own factors.
+    s is bf16 bits [N] or None (s = 1); U [N, r] and V [n_seg, K, r] (or [K, r] for one segment)
+    bf16 bits, or None (r = 0)."""
     N = np.asarray(codes).shape[0]
     idx = np.arange(N) if rows is None else np.asarray(rows)
     y = gemv_nvfp4(codes, scales, ts, x_bf16, seg_end, rows=idx)
@@ -409,20 +411,33 @@ def gemv_nvfp4_lowrank(codes, scales, ts, s_bf16, U_bf16, V_bf16, x_bf16, seg_en
         y = y * bf16_to_f32(np.asarray(s_bf16)[idx]).astype(np.float64)
     if U_bf16 is not None and np.asarray(U_bf16).shape[1] > 0:
         x = bf16_to_f32(x_bf16).astype(np.float64).reshape(-1)
-        t = bf16_to_f32(V_bf16).astype(np.float64).T @ x
-        y = y + bf16_to_f32(np.asarray(U_bf16)[idx]).astype(np.float64) @ t
+        V = bf16_to_f32(np.asarray(V_bf16)).astype(np.float64)
+        V = V.reshape((-1,) + V.shape[-2:])
+        t = np.stack([V[g].T @ x for g in range(V.shape[0])])               # [n_seg, r]
+        seg = row_segment_index(N, seg_end)[idx]
+        U = bf16_to_f32(np.asarray(U_bf16)[idx]).astype(np.float64)
+        y = y + np.sum(U * t[seg], axis=1)
     return y
 
 
-def abs_lowrank(s_bf16, U_bf16, V_bf16, x_bf16, absdot_w0, rows=None) -> np.ndarray:
-    """|s| * sum_k |x_k w0_k| + sum_j |U_j| (sum_k |x_k V_kj|): the magnitude scale of the fp32
-    rounding error of the low-rank product, for any summation order."""
-    idx = slice(None) if rows is None else np.asarray(rows)
+def row_segment_index(N: int, seg_end) -> np.ndarray:
+    """The segment each fused row belongs to."""
+    ends = [N] if seg_end is None else list(seg_end)
+    return np.searchsorted(np.asarray(ends), np.arange(N), side="right")
+
+
+def abs_lowrank(s_bf16, U_bf16, V_bf16, x_bf16, absdot_w0, seg_end=None) -> np.ndarray:
+    """|s| * sum_k |x_k w0_k| + sum_j |U_j| (sum_k |x_k V_g,kj|) for the rows of absdot_w0 (s, U and
+    seg_end describe the same rows): the magnitude scale of the fp32 rounding error of the
+    low-rank product, for any summation order."""
     out = np.asarray(absdot_w0, dtype=np.float64).copy()
     if s_bf16 is not None:
-        out = out * np.abs(bf16_to_f32(np.asarray(s_bf16)[idx]).astype(np.float64))
+        out = out * np.abs(bf16_to_f32(np.asarray(s_bf16)).astype(np.float64))
     if U_bf16 is not None and np.asarray(U_bf16).shape[1] > 0:
         x = np.abs(bf16_to_f32(x_bf16).astype(np.float64)).reshape(-1)
-        t = np.abs(bf16_to_f32(V_bf16).astype(np.float64)).T @ x
-        out = out + np.abs(bf16_to_f32(np.asarray(U_bf16)[idx]).astype(np.float64)) @ t
+        V = np.abs(bf16_to_f32(np.asarray(V_bf16)).astype(np.float64))
+        V = V.reshape((-1,) + V.shape[-2:])
+        t = np.stack([V[g].T @ x for g in range(V.shape[0])])
+        seg = row_segment_index(len(out), seg_end)
+        out = out + np.sum(np.abs(bf16_to_f32(np.asarray(U_bf16)).astype(np.float64)) * t[seg], axis=1)
     return out

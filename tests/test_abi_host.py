@@ -29,6 +29,7 @@ def test_header_declares_every_call():
     names = _declared_functions()
     for n in ["attnq_reconstruct", "attnq_quantize_nvfp4", "attnq_gemv_nvfp4", "attnq_gemv_bf16",
               "attnq_gemm_nvfp4_small_m", "attnq_gemv_nvfp4_glu", "attnq_gemv_nvfp4_lowrank",
+              "attnq_gemv_nvfp4_lowrank_workspace",
               "attnq_status_string"]:
         assert n in names
 
@@ -40,6 +41,18 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(attnq_\w+)", out))
     assert exported == set(_declared_functions())
+
+
+def test_lowrank_workspace_sizes():
+    ws = A.attnq_gemv_nvfp4_lowrank_workspace
+    assert ws(5376, 1, 0) == 0
+    assert ws(5376, 1, 16) == 11 * 16              # chunks of 512 rows
+    assert ws(21504, 1, 16) == 42 * 16
+    assert ws(5376, 3, 64) == 3 * 42 * 64          # chunks of 128 rows
+    assert ws(96, 2, 3) == 2 * 1 * 3               # 2730 rows per chunk
+    assert ws(32, 1, 1) == 1
+    for bad in [(0, 1, 4), (40, 1, 4), (64, 0, 4), (64, 5, 4), (64, 1, 65), (64, 1, -1)]:
+        assert ws(*bad) == -1
 
 
 def test_status_strings():
@@ -154,7 +167,7 @@ def test_gemv_and_gemm_validation():
     assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE, 4, FAKE, FAKE + 2, FAKE, None) == 3    # t 4-byte
     assert lr(ctypes.byref(nv), FAKE + 1, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 3    # s 2-byte
     assert lr(ctypes.byref(nv), FAKE, FAKE + 1, FAKE, 4, FAKE, FAKE, FAKE, None) == 3    # U 2-byte
-    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE + 1, 4, FAKE, FAKE, FAKE, None) == 3    # V 2-byte
+    assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE + 8, 4, FAKE, FAKE, FAKE, None) == 3    # V 16-byte
     assert lr(ctypes.byref(_nv(K=16)), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 2
     g = lib.attnq_gemm_nvfp4_small_m
     assert g(ctypes.byref(nv), FAKE, 17, 64, FAKE, 64, None) == 2                 # M > 16

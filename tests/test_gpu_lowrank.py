@@ -4,8 +4,8 @@
 * r = 0 without s equals attnq_gemv_nvfp4 element for element, and r = 0 with s equals
   fl32(y_gemv * s), in every launch class of the GEMV table (wiring of the epilogue);
 * r = 1 .. 64 against the float64 oracle: every element within the GEMV's fp32 bound on the
-  s-scaled W0 term plus a worst-case fp32 bound on the low-rank term (t = V^T x in chunks of
-  ceil(K / G) then G partials, G = 1024 / r, and r fused multiply-adds), and relative L2
+  s-scaled W0 term plus a worst-case fp32 bound on the low-rank term (the longest chain of
+  roundings through the chunk partials, their reduction and the wave sum), and relative L2
   <= 1e-3 (the contract) and <= 1e-5 (internal gate). U and V are drawn with sigma 0.02 so the
   low-rank term is a few percent of y and a dropped or mis-scaled term cannot hide in the bound;
 * one quantized W0 serves several projections in turn (shared-block reading), a two-segment W0,
@@ -54,13 +54,43 @@ def _factors(N, K, r, layer, proj):
     return s, U, V
 
 
+def _segment_factors(seg_end, K, r, layer):
+    """Per-segment factors of a fused weight: s and U follow the fused rows, V is [n_seg, K, r]."""
+    s, U, V, start = [], [], [], 0
+    for g, end in enumerate(seg_end):
+        sg, Ug, Vg = _factors(end - start, K, r, layer, 1 + g)
+        s.append(sg); U.append(Ug); V.append(Vg)
+        start = end
+    return np.concatenate(s), np.concatenate(U), np.stack(V)
+
+
+def _parts(K, r):
+    """Partial sums per segment in the workspace: one per floor(8192 / r) rows of V."""
+    kc = 8192 // r
+    return -(-K // kc)
+
+
+def _depth(K, r):
+    """fp32 roundings along the longest path of the low-rank term: the chunk sums (4 fused
+    multiply-adds or floor(8192 / r) / (256 // r) + 1 of them), the 8 + 256 // r slot adds, the
+    P partials and 256 // r level sums in the GEMV, the wave sum and the final products."""
+    return 48 + 2 * (256 // r) + _parts(K, r) + 8
+
+
 def _run(A, W, s, U, V, x):
     r = 0 if U is None else U.shape[1]
     y = torch.full((W.N,), float("nan"), dtype=torch.float32, device="cuda")
-    t = torch.full((r,), float("nan"), dtype=torch.float32, device="cuda") if r else None
-    A.attnq_gemv_nvfp4_lowrank(W, dev(s), dev(U), dev(V), dev(x.reshape(-1)), t, y)
+    ws = None
+    if r:
+        n = A.attnq_gemv_nvfp4_lowrank_workspace(W.K, len(W.seg_end), r)
+        assert n == len(W.seg_end) * _parts(W.K, r) * r
+        ws = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    A.attnq_gemv_nvfp4_lowrank(W, dev(s), dev(U), dev(V), dev(x.reshape(-1)), ws, y)
     torch.cuda.synchronize()
-    return host(y), (host(t) if r else None)
+    if not r:
+        return host(y), None
+    t = host(ws).reshape(len(W.seg_end), _parts(W.K, r), r).astype(np.float64).sum(axis=1)   # [n_seg, r]
+    return host(y), t
 
 
 def _plain(A, W, x):
@@ -71,16 +101,16 @@ def _plain(A, W, x):
 
 
 def _check(y, parts, s, U, V, x, K, rows, what):
-    c, sc, ts, seg_end = oracle_quantize(parts, rows=rows)
+    c, sc, ts, _ = oracle_quantize(parts, rows=rows)
+    local = _local_segments(parts, rows)
     r = 0 if U is None else U.shape[1]
     sr = None if s is None else s[rows]
     Ur = None if U is None else U[rows]
-    yref = O.gemv_nvfp4_lowrank(c, sc, ts, sr, Ur, V, x, seg_end=_local_segments(seg_end, parts, rows))
-    ad = O.abs_dot(c, sc, ts, x, _local_segments(seg_end, parts, rows))[0]
+    yref = O.gemv_nvfp4_lowrank(c, sc, ts, sr, Ur, V, x, seg_end=local)
+    ad = O.abs_dot(c, sc, ts, x, local)[0]
     w0 = O.abs_lowrank(sr, None, None, x, ad)
-    lrm = O.abs_lowrank(None, Ur, V, x, np.zeros_like(ad)) if r else np.zeros_like(ad)
-    G = 1024 // r if r else 1
-    depth = -(-K // G) + G + r + 3
+    lrm = O.abs_lowrank(None, Ur, V, x, np.zeros_like(ad), local) if r else np.zeros_like(ad)
+    depth = _depth(K, r) if r else 0
     bound = GEMV_BOUND * w0 + depth * 2.0 ** -24 * lrm + 1e-30
     yg = y[rows].astype(np.float64)
     err = np.abs(yg - yref)
@@ -91,15 +121,12 @@ def _check(y, parts, s, U, V, x, K, rows, what):
     assert rel <= 1e-3, f"{what}: rel-L2 {rel} over the contract"
     assert rel <= 1e-5, f"{what}: rel-L2 {rel} over the internal gate"
     if r:
-        delta = O.gemv_nvfp4_lowrank(c, sc, ts, sr, Ur, V, x, seg_end=_local_segments(seg_end, parts, rows)) - \
-            O.gemv_nvfp4_lowrank(c, sc, ts, sr, None, None, x, seg_end=_local_segments(seg_end, parts, rows))
+        delta = yref - O.gemv_nvfp4_lowrank(c, sc, ts, sr, None, None, x, seg_end=local)
         assert np.linalg.norm(delta) > 4 * np.linalg.norm(bound), f"{what}: low-rank term not visible"
 
 
-def _local_segments(seg_end, parts, rows):
+def _local_segments(parts, rows):
     """oracle_quantize returns only the selected rows; their segment table in that order."""
-    if rows is None:
-        return seg_end
     bounds, n = [], 0
     for p in parts:
         n += p[0].shape[0]
@@ -140,12 +167,11 @@ def test_lowrank_vs_oracle(A, N, K, r):
     rows = None if N * K <= (1 << 24) else np.unique(np.concatenate([
         np.arange(4), np.arange(N - 4, N), np.random.default_rng(N + K).choice(N, 500, replace=False)]))
     _check(y, parts, s, U, V, x, K, np.arange(N) if rows is None else rows, what)
-    # t = V^T x within its own fp32 bound
+    # the workspace's partial sums add up to V^T x within their own fp32 bound
     xv = O.bf16_to_f32(x).astype(np.float64).reshape(-1)
     Vf = O.bf16_to_f32(V).astype(np.float64)
-    G = 1024 // r
-    tb = (-(-K // G) + G) * 2.0 ** -24 * (np.abs(Vf).T @ np.abs(xv))
-    assert np.all(np.abs(t - Vf.T @ xv) <= tb), what
+    tb = _depth(K, r) * 2.0 ** -24 * (np.abs(Vf).T @ np.abs(xv))
+    assert np.all(np.abs(t[0] - Vf.T @ xv) <= tb), what
 
 
 def test_shared_block_serves_several_projections(A):
@@ -170,24 +196,42 @@ def test_repeated_calls_are_bitwise_identical(A):
     y1, t1 = _run(A, W, s, U, V, x)
     y2, t2 = _run(A, W, s, U, V, x)
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
-    assert np.array_equal(t1.view(np.uint32), t2.view(np.uint32))
+    assert np.array_equal(t1, t2)
 
 
-def test_two_segment_block(A):
+def test_two_segment_block_with_per_segment_factors(A):
     N, K, r = 4000, 5376, 16
     say(f"lowrank two segments {N}x{K} rank {r}")
     W, parts = _shared(A, N, K, 74, seg_end=[1500, N])
-    s, U, V = _factors(N, K, r, 74, 1)
+    s, U, V = _segment_factors([1500, N], K, r, 74)
     x = inputs.activation_bf16(1, K, 9, 74, 1)
-    y, _ = _run(A, W, s, U, V, x)
+    y, t = _run(A, W, s, U, V, x)
     _check(y, parts, s, U, V, x, K, np.arange(N), "two-segment block")
+    xv = O.bf16_to_f32(x).astype(np.float64).reshape(-1)
+    for g in range(2):
+        Vf = O.bf16_to_f32(V[g]).astype(np.float64)
+        tb = _depth(K, r) * 2.0 ** -24 * (np.abs(Vf).T @ np.abs(xv))
+        assert np.all(np.abs(t[g] - Vf.T @ xv) <= tb)
+
+
+def test_fused_qkv_31b_like_per_segment_factors(A):
+    seg_end = [4096, 5120, 6144]
+    N, K, r = 6144, 5376, 16
+    say(f"lowrank fused q|k|v {N}x{K} rank {r}")
+    W, parts = _shared(A, N, K, 76, seg_end=seg_end)
+    s, U, V = _segment_factors(seg_end, K, r, 76)
+    x = inputs.activation_bf16(1, K, 9, 76, 1)
+    y, _ = _run(A, W, s, U, V, x)
+    rows = np.unique(np.concatenate([np.arange(4090, 4100), np.arange(5115, 5125), np.arange(N - 4, N),
+                                     np.random.default_rng(76).choice(N, 300, replace=False)]))
+    _check(y, parts, s, U, V, x, K, rows, "fused q|k|v per-segment")
 
 
 def test_empty_weight_is_a_no_op(A):
     say("lowrank N=0")
     W = A.NVFP4Weight.empty(0, 64)
     x = torch.zeros((64,), dtype=torch.int16, device="cuda")
-    t = torch.full((4,), 7.0, dtype=torch.float32, device="cuda")
+    t = torch.full((A.attnq_gemv_nvfp4_lowrank_workspace(64, 1, 4),), 7.0, dtype=torch.float32, device="cuda")
     U = torch.zeros((0, 4), dtype=torch.int16, device="cuda")
     V = torch.zeros((64, 4), dtype=torch.int16, device="cuda")
     A.attnq_gemv_nvfp4_lowrank(W, None, U, V, x, t, torch.empty((0,), dtype=torch.float32, device="cuda"))

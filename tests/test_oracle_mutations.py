@@ -111,31 +111,43 @@ def _lowrank_mutant(monkeypatch, slip):
         sv = OM.bf16_to_f32(np.asarray(s_bf16)).astype(np.float64)
         x = OM.bf16_to_f32(x_bf16).astype(np.float64).reshape(-1)
         U = OM.bf16_to_f32(np.asarray(U_bf16)).astype(np.float64)
-        V = OM.bf16_to_f32(np.asarray(V_bf16)).astype(np.float64)
-        return slip(y, sv, x, U, V)
+        V = OM.bf16_to_f32(np.asarray(V_bf16)).astype(np.float64).reshape((-1, x.size, U.shape[1]))
+        seg = OM.row_segment_index(len(y), seg_end)
+        out = slip(y, sv, x, U, V, seg)
+        return out if rows is None else out[np.asarray(rows)]
     monkeypatch.setattr(OM, "gemv_nvfp4_lowrank", mutated)
     monkeypatch.setattr(O, "gemv_nvfp4_lowrank", mutated)
 
 
+def _delta(U, V, x, seg):
+    return np.sum(U * np.stack([V[g].T @ x for g in range(V.shape[0])])[seg], axis=1)
+
+
 def test_lowrank_scale_on_the_delta_is_caught(monkeypatch):
     import test_oracle_lowrank as PL
-    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V: s * (y + U @ (V.T @ x)))
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V, seg: s * (y + _delta(U, V, x, seg)))
     assert _fails(PL.test_lowrank_equals_exact_rational_sum)
 
 
 def test_lowrank_reversed_factor_rows_are_caught(monkeypatch):
     import test_oracle_lowrank as PL
-    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V: s * y + U @ (V[::-1].T @ x))
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V, seg: s * y + _delta(U, V[:, ::-1], x, seg))
     assert _fails(PL.test_lowrank_equals_exact_rational_sum)
 
 
 def test_lowrank_delta_sign_slip_is_caught(monkeypatch):
     import test_oracle_lowrank as PL
-    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V: s * y - U @ (V.T @ x))
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V, seg: s * y - _delta(U, V, x, seg))
     assert _fails(PL.test_lowrank_equals_exact_rational_sum)
 
 
 def test_lowrank_dropped_rank_is_caught(monkeypatch):
     import test_oracle_lowrank as PL
-    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V: s * y + U[:, :-1] @ (V[:, :-1].T @ x))
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V, seg: s * y + _delta(U[:, :-1], V[:, :, :-1], x, seg))
+    assert _fails(PL.test_lowrank_equals_exact_rational_sum)
+
+
+def test_lowrank_first_segment_factors_everywhere_are_caught(monkeypatch):
+    import test_oracle_lowrank as PL
+    _lowrank_mutant(monkeypatch, lambda y, s, x, U, V, seg: s * y + _delta(U, V, x, np.zeros_like(seg)))
     assert _fails(PL.test_lowrank_equals_exact_rational_sum)
