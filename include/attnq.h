@@ -163,7 +163,7 @@ ATTNQ_API attnq_status attnq_gemv_nvfp4_glu(const attnq_nvfp4* W, const uint16_t
  * row-major, NULL when r == 0 (U may also be NULL when N == 0), 0 <= r <= 64.
  * ws is a caller-owned fp32 workspace of at least attnq_gemv_nvfp4_lowrank_workspace(K, n_seg, r)
  * values (NULL when r == 0); it receives partial sums of V[g]^T x, P per segment, each over
- * floor(8192 / r) consecutive k: ws[(g * P + p) * r + j], P = ceil(K / floor(8192 / r)).
+ * floor(16384 / r) consecutive k: ws[(g * P + p) * r + j], P = ceil(K / floor(16384 / r)).
  * Two kernels in stream order: the partial sums, then the streaming GEMV, which reduces them to
  * t and applies s and U t in its epilogue. fp32 arithmetic; every sum is taken in a fixed order,
  * so repeated calls give identical bits. x and V 16-byte aligned, y and ws 4-byte aligned, s and

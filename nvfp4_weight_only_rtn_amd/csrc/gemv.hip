@@ -69,13 +69,14 @@ __device__ __forceinline__ void store_glu(uint16_t* h, int j, float g, float u, 
 
 // Runtime low-rank epilogue (EPI 2): for a row of segment g,
 //   y[row] = s[row] * (x . weight0[row]) + sum_k U[row][k] t[g][k],  t[g] = V[g]^T x.
-// k_lowrank_part leaves P partial sums of t per segment (one per 16 KB chunk of V); each GEMV
-// workgroup loads its segment's partials right after issuing its weight loads, reduces them to
-// t in LDS after the main loop, and each wave adds U[row] . t across its lanes. Every sum is
-// taken in one fixed order, so the result does not depend on timing or on the launch shape.
-constexpr int kLrThreads = 256;     // threads of the partial-sum kernel and of the t reduction
-constexpr int kLrChunk = 8192;      // V elements behind one partial (16 KB of bf16)
-constexpr int kLrPrefetch = 4;      // partials per thread loaded ahead of the main loop
+// k_lowrank_part leaves P partial sums of t per segment (one per 32 KB chunk of V), laid out
+// part[g][p][k]. Each wave folds them into its rows directly: with n = P r, lane l takes the
+// flat indices i = l, l + 64, ... < n and sums U[row][i mod r] * part[g][i] (a fixed order), and
+// the wave adds its lanes. The one-shot kernels load a lane's first two values right after the
+// weight loads are issued; there is no LDS and no barrier, so the kernel keeps the plain GEMV's
+// shape.
+constexpr int kLrThreads = 256;     // threads of the partial-sum kernel
+constexpr int kLrChunk = 16384;     // V elements behind one partial (32 KB of bf16)
 
 struct LowRank {
   const uint16_t* s;     // [N] bf16 or null (s = 1)
@@ -84,94 +85,74 @@ struct LowRank {
   int r, P;
 };
 
-// t[g][k] in the kernels' order: sum over q < Q of (sum over p = q, q + Q, ... of part[g][p][k]),
-// Q = 256 / r. Used for the rare workgroup whose rows reach into a second segment.
-__device__ __forceinline__ float lr_t_direct(const LowRank& lr, int g, int k) {
-  const int Q = kLrThreads / lr.r;
-  const float* pg = lr.part + (size_t)g * lr.P * lr.r;
-  float t = 0.0f;
-  for (int q = 0; q < Q; ++q) {
-    float a = 0.0f;
-    for (int p = q; p < lr.P; p += Q) a += pg[(size_t)p * lr.r + k];
-    t += a;
-  }
-  return t;
-}
-
-template <int R>
+// Values loaded ahead of the main loop (PF partials per lane and, when PF > 0 and r divides 64,
+// U[row][lane mod r]). They are kept as loaded -- raw bits, converted only at their use after the
+// main loop -- and each load is issued unconditionally, from x when its operand is absent, with
+// the choice made by a uniform select at the use: no branch and no wait sits between these loads
+// and the weight loads issued before them.
+template <int R, int PF>
 struct LrRegs {
-  float pv[kLrPrefetch];   // this thread's partials of segment g0
-  float uv[R];             // U[row][lane] of the wave's rows (lane < r)
-  float sv;                // s of the row this lane stores (lane < R)
-  int g0;                  // segment of the workgroup's first row
+  float pv[PF > 0 ? PF : 1];   // part[g0][min(lane + 64 (ks + KS m), n - 1)]
+  uint32_t ub[R];              // U[row][lane mod r] bits of the wave's rows
+  uint32_t sb;                 // s bits of the row this lane stores (lane < R)
+  int g0;                      // segment of the wave's first row
 };
 
-// Thread (q, k) = (tid / r, tid % r) of the first 256 loads part[g0][p][k] for p = q, q + Q, ...
-template <int R, class RowOf>
-__device__ __forceinline__ void lr_prefetch(LrRegs<R>& st, const LowRank& lr, const SegTable& segs, int wg_first,
-                                            const RowOf& row_of, int lane) {
-  st.g0 = segment_of(segs, wg_first);
-  st.sv = (lr.s != nullptr && lane < R) ? bf16_bits_to_f32(lr.s[row_of(lane)]) : 1.0f;
+template <int R, int PF, int KS, class RowOf>
+__device__ __forceinline__ void lr_prefetch(LrRegs<R, PF>& st, const LowRank& lr, const SegTable& segs,
+                                            const RowOf& row_of, int lane, int ks, const void* dummy) {
+  st.g0 = segment_of(segs, row_of(0));
+  const uint16_t* sp = lr.s != nullptr ? lr.s + row_of(min(lane, R - 1)) : static_cast<const uint16_t*>(dummy);
+  st.sb = *sp;
+  if constexpr (PF > 0) {
+    // distinct dummy addresses (x[m], x[r]; x holds at least 32 elements) keep the compiler from
+    // merging the loads of an absent operand into one load plus register copies, which would wait
+    const int n = lr.P * lr.r;
+    const float* pg = n > 0 ? lr.part + (size_t)st.g0 * n : static_cast<const float*>(dummy);
 #pragma unroll
-  for (int u = 0; u < kLrPrefetch; ++u) st.pv[u] = 0.0f;
+    for (int m = 0; m < PF; ++m) st.pv[m] = pg[n > 0 ? min(lane + 64 * (ks + KS * m), n - 1) : m];
+    // U[row][lane mod r] is only used when r divides 64, i.e. r is a power of two (mask, no division)
+    const bool fixed_k = lr.r > 0 && 64 % lr.r == 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) st.uv[r] = 0.0f;
-  if (lr.r == 0) return;
-  const int tid = threadIdx.x, Q = kLrThreads / lr.r, q = tid / lr.r, k = tid - q * lr.r;
-  const float* pg = lr.part + (size_t)st.g0 * lr.P * lr.r;
-  if (tid < kLrThreads && q < Q) {
-#pragma unroll
-    for (int u = 0; u < kLrPrefetch; ++u)
-      if (q + u * Q < lr.P) st.pv[u] = pg[(size_t)(q + u * Q) * lr.r + k];
-  }
-  if (lane < lr.r) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) st.uv[r] = bf16_bits_to_f32(lr.U[(size_t)row_of(r) * lr.r + lane]);
+    for (int r = 0; r < R; ++r)
+      st.ub[r] = *(fixed_k ? lr.U + (size_t)row_of(r) * lr.r + (lane & (lr.r - 1))
+                           : static_cast<const uint16_t*>(dummy) + r);
   }
 }
 
-// All threads of the workgroup: t of the segments g0 .. segment(wg_last) into tl[g - g0][k].
-template <int R>
-__device__ __forceinline__ void lr_reduce(const LrRegs<R>& st, const LowRank& lr, const SegTable& segs, int wg_last,
-                                          float* l1, float* tl) {
-  if (lr.r == 0) return;
-  const int tid = threadIdx.x, Q = kLrThreads / lr.r, q = tid / lr.r, k = tid - q * lr.r;
-  if (tid < kLrThreads) {
-    float a = 0.0f;
-    if (q < Q) {
-#pragma unroll
-      for (int u = 0; u < kLrPrefetch; ++u) a += st.pv[u];
-      const float* pg = lr.part + (size_t)st.g0 * lr.P * lr.r;
-      for (int p = q + kLrPrefetch * Q; p < lr.P; p += Q) a += pg[(size_t)p * lr.r + k];
-    }
-    l1[tid] = a;
-  }
-  __syncthreads();
-  if (tid < lr.r) {
-    float t = 0.0f;
-    for (int qq = 0; qq < Q; ++qq) t += l1[qq * lr.r + tid];
-    tl[tid] = t;
-    const int g_last = segment_of(segs, wg_last);
-    for (int g = st.g0 + 1; g <= g_last; ++g) tl[(g - st.g0) * 64 + tid] = lr_t_direct(lr, g, tid);
-  }
-  __syncthreads();
-}
-
-// d[r] = U[row_r] . t[segment of row_r], summed across the wave (every lane gets the sums).
-template <int R, class RowOf>
-__device__ __forceinline__ void lr_row_terms(const LrRegs<R>& st, const LowRank& lr, const SegTable& segs,
-                                             const float* tl, const RowOf& row_of, int lane, float* d) {
+// d[r] = sum over the wave's indices i < P r of U[row_r][i mod r] * part[g][i] (g the row's
+// segment): lane l of K slice ks (of KS) takes i = l + 64 (ks + KS m), m = 0, 1, ..., in that
+// order, then the wave adds its lanes; every lane gets the sums. The KS slices' sums are added
+// in slice order by the caller.
+template <int R, int PF, int KS, class RowOf>
+__device__ __forceinline__ void lr_row_terms(const LrRegs<R, PF>& st, const LowRank& lr, const SegTable& segs,
+                                             const RowOf& row_of, int lane, int ks, float* d) {
+  const int n = lr.P * lr.r;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    const int row = row_of(r);
+    const uint16_t* u = lr.U + (size_t)row * lr.r;
+    const int g = segment_of(segs, row);
+    const float* pg = lr.part + (size_t)g * n;
     float c = 0.0f;
-    if (lane < lr.r) c = st.uv[r] * tl[(segment_of(segs, row_of(r)) - st.g0) * 64 + lane];
+    if (n > 0) {
+      if (PF > 0 && g == st.g0 && 64 % lr.r == 0) {
+        const float uk = bf16_bits_to_f32((uint16_t)st.ub[r]);
+#pragma unroll
+        for (int m = 0; m < (PF > 0 ? PF : 1); ++m)
+          if (lane + 64 * (ks + KS * m) < n) c = __builtin_fmaf(uk, st.pv[m], c);
+        for (int i = lane + 64 * (ks + KS * PF); i < n; i += 64 * KS) c = __builtin_fmaf(uk, pg[i], c);
+      } else {
+        for (int i = lane + 64 * ks; i < n; i += 64 * KS) c = __builtin_fmaf(bf16_bits_to_f32(u[i % lr.r]), pg[i], c);
+      }
+    }
     d[r] = wave_sum(c);
   }
 }
 
-__device__ __forceinline__ float lr_finish(float v, float ts, float s, float d) {
+__device__ __forceinline__ float lr_finish(float v, float ts, const LowRank& lr, uint32_t s_bits, float d) {
   v *= ts;
-  v *= s;
+  v *= lr.s != nullptr ? bf16_bits_to_f32((uint16_t)s_bits) : 1.0f;
   return v + d;
 }
 
@@ -201,9 +182,6 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-  [[maybe_unused]] LrRegs<R> lrs;
-  [[maybe_unused]] const int wg_first = blockIdx.x * kRowGroups * R;
-  if constexpr (EPI == 2) lr_prefetch<R>(lrs, lr, segs, wg_first, row_of, lane);
 
   for (int c = c_begin + lane; c < c_end; c += 64) {
     const u32x4* xp = reinterpret_cast<const u32x4*>(x + (size_t)c * kChunkElems);
@@ -222,15 +200,16 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
     for (int r = 0; r < R; ++r) acc[r] = chunk_dot(cv[r], sv[r], xw, acc[r]);
   }
 
+  // long rows: the low-rank operands are loaded after the main loop, all at once (holding them
+  // across the loop would cost the stream occupancy)
+  [[maybe_unused]] LrRegs<R, 4> lrs;
+  if constexpr (EPI == 2) lr_prefetch<R, 4, KSPLIT>(lrs, lr, segs, row_of, lane, ks, x);
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
   [[maybe_unused]] float lrd = 0.0f;
   if constexpr (EPI == 2) {
-    __shared__ float lr_l1[kLrThreads];
-    __shared__ float lr_t[ATTNQ_MAX_SEGMENTS * 64];
-    lr_reduce<R>(lrs, lr, segs, min(N, wg_first + kRowGroups * R) - 1, lr_l1, lr_t);
     float d[R];
-    lr_row_terms<R>(lrs, lr, segs, lr_t, row_of, lane, d);
+    lr_row_terms<R, 4, KSPLIT>(lrs, lr, segs, row_of, lane, ks, d);
     lrd = d[0];
 #pragma unroll
     for (int r = 1; r < R; ++r) lrd = (lane == r) ? d[r] : lrd;
@@ -244,22 +223,31 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 #pragma unroll
       for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
       const int row = row0 + lane;
-      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lrs.sv, lrd)
+      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lr, lrs.sb, lrd)
                                      : v * tensor_scale[segment_of(segs, row)];
     }
   } else {
     __shared__ float part[4][R];
+    [[maybe_unused]] __shared__ float partd[EPI == 2 ? 4 : 1][R];
     if (lane == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) part[wave][r] = acc[r];
+    }
+    if constexpr (EPI == 2) {
+      if (lane < R) partd[wave][lane] = lrd;
     }
     __syncthreads();
     if (ks == 0 && lane < R) {
       float v = 0.0f;
 #pragma unroll
       for (int s = 0; s < KSPLIT; ++s) v += part[wave + s][lane];
+      if constexpr (EPI == 2) {
+        lrd = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KSPLIT; ++s) lrd += partd[wave + s][lane];
+      }
       const int row = row0 + lane;
-      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lrs.sv, lrd)
+      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lr, lrs.sb, lrd)
                                      : v * tensor_scale[segment_of(segs, row)];
     }
   }
@@ -314,9 +302,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
       sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
     }
   }
-  [[maybe_unused]] LrRegs<R> lrs;
-  [[maybe_unused]] const int wg_first = blockIdx.x * kRowGroups * R;
-  if constexpr (EPI == 2) lr_prefetch<R>(lrs, lr, segs, wg_first, row_of, lane);
+  [[maybe_unused]] LrRegs<R, 2> lrs;
+  if constexpr (EPI == 2) lr_prefetch<R, 2, KSPLIT>(lrs, lr, segs, row_of, lane, ks, x);
   if constexpr (XFIRST) {
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
@@ -352,11 +339,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
   [[maybe_unused]] float lrd = 0.0f;
   if constexpr (EPI == 2) {
-    __shared__ float lr_l1[kLrThreads];
-    __shared__ float lr_t[ATTNQ_MAX_SEGMENTS * 64];
-    lr_reduce<R>(lrs, lr, segs, min(N, wg_first + kRowGroups * R) - 1, lr_l1, lr_t);
     float d[R];
-    lr_row_terms<R>(lrs, lr, segs, lr_t, row_of, lane, d);
+    lr_row_terms<R, 2, KSPLIT>(lrs, lr, segs, row_of, lane, ks, d);
     lrd = d[0];
 #pragma unroll
     for (int r = 1; r < R; ++r) lrd = (lane == r) ? d[r] : lrd;
@@ -369,22 +353,31 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
 #pragma unroll
       for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
       const int row = row0 + lane;
-      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lrs.sv, lrd)
+      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lr, lrs.sb, lrd)
                                      : v * tensor_scale[segment_of(segs, row)];
     }
   } else {
     __shared__ float part[WAVES][R];
+    [[maybe_unused]] __shared__ float partd[EPI == 2 ? WAVES : 1][R];
     if (lane == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) part[wave][r] = acc[r];
+    }
+    if constexpr (EPI == 2) {
+      if (lane < R) partd[wave][lane] = lrd;
     }
     __syncthreads();
     if (ks == 0 && lane < R) {
       float v = 0.0f;
 #pragma unroll
       for (int k2 = 0; k2 < KSPLIT; ++k2) v += part[wave + k2][lane];
+      if constexpr (EPI == 2) {
+        lrd = 0.0f;
+#pragma unroll
+        for (int k2 = 0; k2 < KSPLIT; ++k2) lrd += partd[wave + k2][lane];
+      }
       const int row = row0 + lane;
-      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lrs.sv, lrd)
+      if (row < N) y[row] = EPI == 2 ? lr_finish(v, tensor_scale[segment_of(segs, row)], lr, lrs.sb, lrd)
                                      : v * tensor_scale[segment_of(segs, row)];
     }
   }
@@ -431,34 +424,39 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
 }
 
 // part[g][p][k] = sum over the rows j of chunk p of x[j] V[g][j][k] (V [n_seg][K][r] bf16), one
-// workgroup per (chunk, segment); a chunk is floor(8192 / r) rows of V. For r a power of two a
-// thread loads four 16-byte pieces of the chunk, and its element i always falls in column
-// (8 tid + i) mod r, so it keeps eight column sums; the workgroup then adds slots of one column
-// in a fixed tree. Other ranks take one column per thread and 2-byte loads.
+// workgroup per (chunk, segment); a chunk is floor(16384 / r) rows of V. For r a power of two a
+// thread loads eight 16-byte pieces of the chunk (issued before x is staged), and its element i
+// always falls in column (8 tid + i) mod r, so it keeps eight column sums; the workgroup then
+// adds the slots of one column in a fixed tree. Other ranks take one column per thread.
 __global__ __launch_bounds__(kLrThreads) void k_lowrank_part(const uint16_t* __restrict__ V,
                                                              const uint16_t* __restrict__ x, float* __restrict__ part,
                                                              int K, int r, int P) {
+  constexpr int kRounds = kLrChunk / (kLrThreads * 8);
   __shared__ float l1[kLrThreads * 8];
   __shared__ uint16_t xl[kLrChunk];
   const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int KC = kLrChunk / r, j0 = p * KC, rows = min(KC, K - j0);
   const uint16_t* Vc = V + ((size_t)g * K + j0) * r;
-  for (int j = tid; j < rows; j += kLrThreads) xl[j] = x[j0 + j];
-  __syncthreads();
   float* out = part + ((size_t)g * P + p) * r;
-  if ((r & (r - 1)) == 0) {
-    const int sh = __builtin_ctz(r), E = rows * r;          // E is a multiple of 32
-    u32x4 v[4];
+  const bool pow2 = (r & (r - 1)) == 0;
+  const int E = rows * r;                                     // a multiple of 32 when r is a power of two
+  u32x4 v[kRounds];
+  if (pow2) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < kRounds; ++m) {
       const int e0 = (m * kLrThreads + tid) * 8;
       v[m] = e0 < E ? *reinterpret_cast<const u32x4*>(Vc + e0) : u32x4{0u, 0u, 0u, 0u};
     }
+  }
+  for (int j = tid; j < rows; j += kLrThreads) xl[j] = x[j0 + j];
+  __syncthreads();
+  if (pow2) {
+    const int sh = __builtin_ctz(r);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < kRounds; ++m) {
       const int e0 = (m * kLrThreads + tid) * 8;
       if (e0 < E) {
         const uint32_t w[4] = {v[m].x, v[m].y, v[m].z, v[m].w};

@@ -46,10 +46,10 @@ def test_library_exports_every_declared_symbol():
 def test_lowrank_workspace_sizes():
     ws = A.attnq_gemv_nvfp4_lowrank_workspace
     assert ws(5376, 1, 0) == 0
-    assert ws(5376, 1, 16) == 11 * 16              # chunks of 512 rows
-    assert ws(21504, 1, 16) == 42 * 16
-    assert ws(5376, 3, 64) == 3 * 42 * 64          # chunks of 128 rows
-    assert ws(96, 2, 3) == 2 * 1 * 3               # 2730 rows per chunk
+    assert ws(5376, 1, 16) == 6 * 16               # chunks of 1024 rows
+    assert ws(21504, 1, 16) == 21 * 16
+    assert ws(5376, 3, 64) == 3 * 21 * 64          # chunks of 256 rows
+    assert ws(96, 2, 3) == 2 * 1 * 3               # 5461 rows per chunk
     assert ws(32, 1, 1) == 1
     for bad in [(0, 1, 4), (40, 1, 4), (64, 0, 4), (64, 5, 4), (64, 1, 65), (64, 1, -1)]:
         assert ws(*bad) == -1

@@ -65,16 +65,17 @@ def _segment_factors(seg_end, K, r, layer):
 
 
 def _parts(K, r):
-    """Partial sums per segment in the workspace: one per floor(8192 / r) rows of V."""
-    kc = 8192 // r
+    """Partial sums per segment in the workspace: one per floor(16384 / r) rows of V."""
+    kc = 16384 // r
     return -(-K // kc)
 
 
 def _depth(K, r):
-    """fp32 roundings along the longest path of the low-rank term: the chunk sums (4 fused
-    multiply-adds or floor(8192 / r) / (256 // r) + 1 of them), the 8 + 256 // r slot adds, the
-    P partials and 256 // r level sums in the GEMV, the wave sum and the final products."""
-    return 48 + 2 * (256 // r) + _parts(K, r) + 8
+    """fp32 roundings along the longest path of the low-rank term: the chunk sums (8 fused
+    multiply-adds, or up to floor(16384 / r) / (256 // r) + 1 of them), the 8 + 256 // r slot adds,
+    a lane's ceil(P r / 64) <= P fused multiply-adds in the GEMV, the wave sum and the final
+    products."""
+    return 96 + 2 * (256 // r) + _parts(K, r) + 9
 
 
 def _run(A, W, s, U, V, x):
