@@ -31,6 +31,15 @@ What it computes, and where each step is defined:
   evaluated in float64 on the float64 GEMV outputs and rounded once to bf16
   (PARITY PINNED by closed forms, odd-part identities and a library
   cross-check in tests/test_oracle_glu.py).
+* The runtime low-rank product over a shared NVFP4 block, ``y = s * (x .
+  deq(W0)^T) + U (V_g^T x)`` with the weight never rebuilt -- "Throughput",
+  "The runtime reconstruction path does not reach dense parity" (W0 and the
+  low-rank delta applied on every forward pass); weightless "GPU and cache
+  acceleration", "Custom-op kernel" (the W0 dot product and the low-rank
+  delta fused) and "Future work / Trained weight sharing" (a shared NVFP4 W0
+  plus a bf16 low-rank pair). Each segment of a fused weight is one
+  projection with its own factors (PARITY PINNED by exact rational sums and
+  mutations in tests/test_oracle_lowrank.py and test_oracle_mutations.py).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
