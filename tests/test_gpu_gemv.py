@@ -59,6 +59,16 @@ def test_gemv_ragged_shapes(A, N, K):
     _gemv_case(A, [b], K, x, f"gemv ragged {N}x{K}")
 
 
+# long rows (K = 21504, the down projection's K split over a workgroup): one row, an odd row count
+# (rows past N clamped) and a two-segment weight whose boundary falls inside a workgroup's rows
+@pytest.mark.parametrize("segs", [(1,), (301,), (1501, 2596)])
+def test_gemv_long_rows_segments(A, segs):
+    K = 21504
+    bs = [inputs.theta_bundle(n, K, 0, cfg=9, layer=34, proj=i, passthrough=True) for i, n in enumerate(segs)]
+    x = inputs.activation_bf16(1, K, 9, 34, len(segs))
+    _gemv_case(A, bs, K, x, f"gemv long rows {segs}x{K}")
+
+
 def test_gemv_one_hot_columns_are_exact(A):
     N, K = 96, 2048
     b = inputs.theta_bundle(N, K, 0, cfg=9, layer=31, proj=0, passthrough=True)
