@@ -4,18 +4,20 @@
 // Matrix-core path, v_mfma_f32_16x16x32_bf16. Operand layout for lane l = 16 g + i (checked on
 // gfx950): A[i][8 g + e], B[8 g + e][i] for e = 0..7, and D[4 g + v][i] for v = 0..3.
 //
-// Weights (B operand). Lane (g, i) of row tile t owns 32 contiguous code bytes (64 codes) of
-// weight row 16 t + i in every 256-element superchunk, so the four lane groups of a row read one
-// whole 128-byte line. Dword m of those 32 bytes feeds MFMA m (m = 0..7): it covers superchunk
-// positions 64 g + 8 m + e, which lie in block 4 g + m/2.
+// Weights (B operand). Lane (g, i) of row tile t owns code bytes 16 g .. 16 g + 15 and 64 + 16 g ..
+// 64 + 16 g + 15 of weight row 16 t + i in every 256-element superchunk (128 code bytes), so each
+// 16-byte load instruction reads one contiguous 64-byte half line per row. The K order inside an
+// MFMA is free as long as A and B agree: dword m of the lane's 32 bytes feeds MFMA m (m = 0..7)
+// and covers superchunk positions 32 g + 8 (m % 4) + 128 (m / 4) + e, in block
+// 2 g + (m / 2) % 2 + 8 (m / 4).
 //
 // M <= 4, block scales as MFMA rows (k_gemm_small_m_mfma). Codes are decoded to bf16 without
 // their scale (v_cvt_scalef32_pk_bf16_fp4, exact). An MFMA sums over all 32 of its K positions,
 // which belong to four different scale blocks (one per lane group g); to keep the blocks apart,
 // the A row index carries (token, block slot): A[4 tau + b][8 g + e] = X[token tau][pos] when
 // b == g and 0 otherwise. After MFMAs 2 h and 2 h + 1, output row 4 tau + v holds the
-// exact-product fp32 partial dot product of token tau over block 4 v + h, and lane (tau, row)
-// applies the E4M3 scale of (row, block 4 v + h) with one FMA per v. (The template also runs
+// exact-product fp32 partial dot product of token tau over the block lane group v holds in pair h,
+// 2 v + h % 2 + 8 (h / 2), and lane (tau, row) applies that block's E4M3 scale with one FMA per v. (The template also runs
 // P = ceil(M / 4) passes over the same decoded weights for larger M; the launcher uses P = 1.)
 //
 // 4 < M <= 16, tokens as MFMA rows (k_gemm_small_m_scaled). Codes are decoded to fp32,
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int row = min(row0 + 16 * t + i, N - 1);
-    crow[t] = codes + (size_t)row * code_pitch + 32 * g;
+    crow[t] = codes + (size_t)row * code_pitch + 16 * g;
     srow[t] = scales + (size_t)row * scale_pitch;
   }
   // A operand source: lane (g, i) carries token 4 p + (i >> 2) when (i & 3) == g.
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
     for (int t = 0; t < RT; ++t) {
       const u32x4* cp = reinterpret_cast<const u32x4*>(crow[t] + (size_t)sc * (kSuper / 2));
       cw[t][0] = __builtin_nontemporal_load(cp);
-      cw[t][1] = __builtin_nontemporal_load(cp + 1);
+      cw[t][1] = __builtin_nontemporal_load(cp + 4);
       sw[t] = load_scales16(srow[t] + (size_t)sc * (kSuper / kBlock), scales_a16);
     }
   };
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         if (act[p]) {
-          const u32x4* xp = reinterpret_cast<const u32x4*>(xrow[p] + (size_t)sc * kSuper + 64 * g + 16 * h);
+          const u32x4* xp = reinterpret_cast<const u32x4*>(xrow[p] + (size_t)sc * kSuper + 32 * g + 16 * (h & 1) + 128 * (h >> 1));
           xa[p][0] = xp[0];
           xa[p][1] = xp[1];
         }
@@ -146,10 +148,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
       for (int t = 0; t < RT; ++t) {
         const bf16x8 b0 = decode8(word(cw[t][h >> 1], 2 * (h & 1)));
         const bf16x8 b1 = decode8(word(cw[t][h >> 1], 2 * (h & 1) + 1));
-        // scales of blocks 4 v + h, v = 0..3: byte h of scale dword v
+        // scale of the block that lane group v holds in pair h: 2 v + (h & 1) + 8 (h >> 1)
         float s[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s[v] = e4m3_byte(word(sw[t], v), h);
+        for (int v = 0; v < 4; ++v) {
+          const int b = 2 * v + (h & 1) + 8 * (h >> 1);
+          s[v] = e4m3_byte(word(sw[t], b >> 2), b & 3);
+        }
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[p][0]), b0, zero4, 0, 0, 0);
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
     }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const uint8_t* cbase = crow[t] - 32 * g;
+      const uint8_t* cbase = crow[t] - 16 * g;
       const uint32_t w = *reinterpret_cast<const uint32_t*>(cbase + (size_t)ch * 16 + 4 * g);
       const uint32_t sv = *reinterpret_cast<const uint16_t*>(srow[t] + (size_t)ch * 2);
       const float s_lo = __builtin_amdgcn_cvt_f32_fp8((int)sv, 0), s_hi = __builtin_amdgcn_cvt_f32_fp8((int)sv, 1);
@@ -261,8 +266,8 @@ __device__ __forceinline__ bf16x8 decode8_scaled(uint32_t w, float s) {
 // Tokens-as-rows variant for 4 < M <= 16: A[i][8 g + e] = X[token i][pos] (tokens >= M read as
 // zero), B = codes times their block scale in bf16 (exact, see decode8_scaled). All MFMAs of a
 // row tile accumulate into one 16 x 16 tile, D[4 g + v][i] = token 4 g + v, weight row i. Lane
-// (g, i) needs one scale byte per MFMA pair: dword g of the row's 16 superchunk scale bytes holds
-// blocks 4 g .. 4 g + 3, and MFMA m uses byte m / 2.
+// (g, i) needs one scale byte per MFMA pair h: block 2 g + h % 2 + 8 (h / 2), i.e. the row's
+// superchunk scale bytes 2 g, 2 g + 1, 2 g + 8 and 2 g + 9.
 template <int RT>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_scaled(const uint8_t* __restrict__ codes,
                                                                        const uint8_t* __restrict__ scales,
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_scaled(const ui
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int row = min(row0 + 16 * t + i, N - 1);
-    crow[t] = codes + (size_t)row * code_pitch + 32 * g;
+    crow[t] = codes + (size_t)row * code_pitch + 16 * g;
     srow[t] = scales + (size_t)row * scale_pitch;
   }
   const bool act = i < M;
@@ -298,16 +303,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_scaled(const ui
     for (int t = 0; t < RT; ++t) {
       const u32x4* cp = reinterpret_cast<const u32x4*>(crow[t] + (size_t)sc * (kSuper / 2));
       cw[t][0] = __builtin_nontemporal_load(cp);
-      cw[t][1] = __builtin_nontemporal_load(cp + 1);
-      const uint16_t* sp = reinterpret_cast<const uint16_t*>(srow[t] + (size_t)sc * (kSuper / kBlock) + 4 * g);
-      sw[t] = sp[0] | ((uint32_t)sp[1] << 16);
+      cw[t][1] = __builtin_nontemporal_load(cp + 4);
+      const uint16_t* sp = reinterpret_cast<const uint16_t*>(srow[t] + (size_t)sc * (kSuper / kBlock) + 2 * g);
+      sw[t] = sp[0] | ((uint32_t)sp[4] << 16);               // blocks 2 g, 2 g + 1, 2 g + 8, 2 g + 9
     }
   };
   auto compute = [&](const u32x4 (&cw)[RT][2], const uint32_t (&sw)[RT], int sc) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       if (act) {
-        const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (size_t)sc * kSuper + 64 * g + 16 * h);
+        const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + (size_t)sc * kSuper + 32 * g + 16 * (h & 1) + 128 * (h >> 1));
         xa[0] = xp[0];
         xa[1] = xp[1];
       }
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_scaled(const ui
     if (act) xt = *reinterpret_cast<const u32x4*>(xrow + (size_t)ch * kChunkElems + 8 * g);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(crow[t] - 32 * g + (size_t)ch * 16 + 4 * g);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(crow[t] - 16 * g + (size_t)ch * 16 + 4 * g);
       const float s = __builtin_amdgcn_cvt_f32_fp8((int)srow[t][(size_t)ch * 2 + (g >> 1)], 0);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xt), decode8_scaled(w, s), acc[t], 0, 0, 0);
     }
