@@ -77,7 +77,7 @@ def test_lowrank_four_segments(A):
     V = np.stack([inputs.normal_bf16((K, r), 0.02, 9, 92, 10 + g, inputs.T_V) for g in range(4)])
     x = inputs.activation_bf16(1, K, 9, 92, 0)
     y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty((A.attnq_gemv_nvfp4_lowrank_workspace(K, 4, r),), dtype=torch.float32, device="cuda")
+    ws = torch.zeros((A.attnq_gemv_nvfp4_lowrank_workspace(K, 4, r),), dtype=torch.float32, device="cuda")
     A.attnq_gemv_nvfp4_lowrank(W, dev(s), dev(U), dev(V), dev(x.reshape(-1)), ws, y)
     torch.cuda.synchronize()
     yref = O.gemv_nvfp4_lowrank(c, sc, t, s, U, V, x, seg_end)

@@ -200,6 +200,25 @@ def test_repeated_calls_are_bitwise_identical(A):
     assert np.array_equal(t1, t2)
 
 
+@pytest.mark.parametrize("N,K,r", [(1000, 2080, 16), (6144, 5376, 16), (16400, 5376, 8), (500, 8192, 32),
+                                   (300, 21504, 16), (77, 16416, 3)])
+def test_one_workspace_across_calls_with_new_inputs(A, N, K, r):
+    """Calls that reuse one workspace with a different x each time must each equal a call on a
+    fresh workspace, bit for bit: no partial sum of an earlier call may be read from any cache."""
+    what = f"lowrank reused workspace {N}x{K} rank {r}"
+    say(what)
+    W, _ = _shared(A, N, K, 78)
+    s, U, V = _factors(N, K, r, 78, 1)
+    ws = torch.zeros((A.attnq_gemv_nvfp4_lowrank_workspace(K, 1, r),), dtype=torch.float32, device="cuda")
+    for i in (0, 1, 2, 0):
+        x = inputs.activation_bf16(1, K, 9, 78, i)
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        A.attnq_gemv_nvfp4_lowrank(W, dev(s), dev(U), dev(V), dev(x.reshape(-1)), ws, y)
+        torch.cuda.synchronize()
+        y_fresh, _ = _run(A, W, s, U, V, x)
+        assert np.array_equal(host(y).view(np.uint32), y_fresh.view(np.uint32)), f"{what}, input {i}"
+
+
 def test_two_segment_block_with_per_segment_factors(A):
     N, K, r = 4000, 5376, 16
     say(f"lowrank two segments {N}x{K} rank {r}")
