@@ -29,7 +29,9 @@
 // product; the tensor scale is applied last. A workgroup owns 2 x 16 weight rows; its waves split
 // the superchunks of K, keep the next superchunk's weights in flight while computing the current
 // one, and meet in LDS at the end. Rows past N and tokens past M are clamped or masked and never
-// stored.
+// stored. The M <= 4 kernel also loads each superchunk's X together with its weights, one
+// superchunk ahead: load counters complete in order, so X loaded inside the compute step (after
+// the next superchunk's weight loads) would make every wait for X a wait for those weights too.
 #include "attnq_device.h"
 #include "launch.h"
 
@@ -40,7 +42,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kSuper = 256;        // K elements per superchunk: 128 code bytes and 16 scale bytes per row
-constexpr int kMaxWaves = 16;      // K split: waves of one workgroup over the same rows
+constexpr int kMaxWaves = 12;      // K split: waves of one workgroup over the same rows (the launch bound
+                                   // of 768 threads leaves 168 VGPRs per lane for the operand buffers)
 
 // 8 E2M1 codes (even element in the low nibble) -> 8 bf16, exact.
 __device__ __forceinline__ bf16x8 decode8(uint32_t w) {
@@ -97,14 +100,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
     crow[t] = codes + (size_t)row * code_pitch + 16 * g;
     srow[t] = scales + (size_t)row * scale_pitch;
   }
-  // A operand source: lane (g, i) carries token 4 p + (i >> 2) when (i & 3) == g.
+  // A operand source: lane (g, i) carries token 4 p + (i >> 2) when (i & 3) == g. X is read through
+  // a buffer resource bounded to its extent: the other lanes use an offset past the end, which
+  // returns zeros without a memory request, so every X load is unconditional.
   bool act[P];
   const uint16_t* xrow[P];
+  const int x_bytes = ((M - 1) * ldx + K) * 2;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, x_bytes,
+                                                                        0x00020000);
+  int xoff[P];                 // byte offset of this lane's X piece in superchunk 0
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int tok = 4 * p + (i >> 2);
     act[p] = ((i & 3) == g) && tok < M;
     xrow[p] = X + (size_t)min(tok, M - 1) * ldx;
+    xoff[p] = act[p] ? (tok * ldx + 32 * g) * 2 : x_bytes;
   }
 
   float acc[P][RT];
@@ -113,17 +123,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[p][t] = 0.0f;
 
-  // A operands stay zero in inactive lanes: they are written only under act[p].
-  u32x4 xa[P][2];
-#pragma unroll
-  for (int p = 0; p < P; ++p) xa[p][0] = xa[p][1] = u32x4{0u, 0u, 0u, 0u};
-
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
   const int nsc = K / kSuper;
   const int s_begin = wave * per, s_end = min(nsc, s_begin + per);
 
-  // Code and scale loads of superchunk sc into one of two register buffers.
-  auto load_w = [&](u32x4 (&cw)[RT][2], u32x4 (&sw)[RT], int sc) {
+  // Code and scale loads of superchunk sc into one of two register buffers, then its X pieces
+  // (MFMAs 2 h and 2 h + 1 take positions 32 g + 16 (h % 2) + 128 (h / 2) .. + 15). Each
+  // superchunk's X is issued with its weights, ahead of the next superchunk's loads, so that the
+  // wait for it (counters complete in order) never waits for the next superchunk's weights.
+  auto load_w = [&](u32x4 (&cw)[RT][2], u32x4 (&sw)[RT], u32x4 (&xa)[P][4][2], int sc) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const u32x4* cp = reinterpret_cast<const u32x4*>(crow[t] + (size_t)sc * (kSuper / 2));
@@ -131,19 +139,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
       cw[t][1] = __builtin_nontemporal_load(cp + 4);
       sw[t] = load_scales16(srow[t] + (size_t)sc * (kSuper / kBlock), scales_a16);
     }
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int o = xoff[p] + (sc * kSuper + 16 * (h & 1) + 128 * (h >> 1)) * 2;
+        xa[p][h][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, o, 0, 0));
+        xa[p][h][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, o + 16, 0, 0));
+      }
   };
-  auto compute = [&](const u32x4 (&cw)[RT][2], const u32x4 (&sw)[RT], int sc) {
+  auto compute = [&](const u32x4 (&cw)[RT][2], const u32x4 (&sw)[RT], const u32x4 (&xa)[P][4][2], int sc) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      // X of MFMAs 2 h and 2 h + 1: positions 64 g + 16 h .. + 15 of the superchunk
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        if (act[p]) {
-          const u32x4* xp = reinterpret_cast<const u32x4*>(xrow[p] + (size_t)sc * kSuper + 32 * g + 16 * (h & 1) + 128 * (h >> 1));
-          xa[p][0] = xp[0];
-          xa[p][1] = xp[1];
-        }
-      }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const bf16x8 b0 = decode8(word(cw[t][h >> 1], 2 * (h & 1)));
@@ -157,8 +164,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
         }
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[p][0]), b0, zero4, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[p][1]), b1, d, 0, 0, 0);
+          f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[p][h][0]), b0, zero4, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[p][h][1]), b1, d, 0, 0, 0);
           float a = acc[p][t];
           a = __builtin_fmaf(d.x, s[0], a);
           a = __builtin_fmaf(d.y, s[1], a);
@@ -169,16 +176,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_mfma(const uint
       }
     }
   };
-  // Two-stage pipeline: the weights of the next superchunk are in flight while this one computes.
+  // Two-stage pipeline: the weights and X of the next superchunk are in flight while this one computes.
   if (s_begin < s_end) {
     u32x4 cwa[RT][2], swa[RT], cwb[RT][2], swb[RT];
-    load_w(cwa, swa, s_begin);
+    u32x4 xaa[P][4][2], xab[P][4][2];
+    load_w(cwa, swa, xaa, s_begin);
     for (int sc = s_begin; sc < s_end; sc += 2) {
-      if (sc + 1 < s_end) load_w(cwb, swb, sc + 1);
-      compute(cwa, swa, sc);
+      if (sc + 1 < s_end) load_w(cwb, swb, xab, sc + 1);
+      compute(cwa, swa, xaa, sc);
       if (sc + 1 < s_end) {
-        if (sc + 2 < s_end) load_w(cwa, swa, sc + 2);
-        compute(cwb, swb, sc + 1);
+        if (sc + 2 < s_end) load_w(cwa, swa, xaa, sc + 2);
+        compute(cwb, swb, xab, sc + 1);
       }
     }
   }
