@@ -560,13 +560,14 @@ void launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, in
 // Launch table (timed per shape on MI355X, 31B-like shapes streamed cold): rows of up to 6144
 // elements use the one-shot kernel. The fused gate|up (43008 x 5376) stages x in LDS after its
 // weight loads; q|k|v (6144 x 5376, one row per wave) and o (5376 x 4096, two rows per wave,
-// two steps) stage x first. Long rows (the down projection, K = 21504) split K over the four
-// waves of a workgroup in the loop kernel.
+// two steps) stage x first. Long rows (the down projection, K = 21504) use the loop kernel with
+// four rows per wave and K split over two waves (two row groups per workgroup): inside the
+// token stream this beat splits of 1 and 4 and 2 or 8 rows per wave.
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
   if (W.N == 0) return hipSuccess;
   const int cpr = W.K / 32;
   if (W.K >= 16384)
-    launch_nvfp4_loop<4, 4>(W, x, y, stream);
+    launch_nvfp4_loop<4, 2>(W, x, y, stream);
   else if (cpr <= 128)
     launch_nvfp4_oneshot<2, 1, 2, true, 4, true, 2>(W, x, y, stream);    // K <= 4096: two steps per row (x: 2 x 256 >= K/8)
   else if (cpr <= 192 && W.N >= 16384)
@@ -595,7 +596,7 @@ hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, co
   }
   const int cpr = W.K / 32;
   if (W.K >= 16384)
-    launch_lr_loop<4, 4>(W, x, y, lr, stream);
+    launch_lr_loop<4, 2>(W, x, y, lr, stream);
   else if (cpr <= 128)
     launch_lr_oneshot<2, 1, 2, true, 4, true, 2>(W, x, y, lr, stream);
   else if (cpr <= 192 && W.N >= 16384)
