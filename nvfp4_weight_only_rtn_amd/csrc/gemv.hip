@@ -394,6 +394,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll 4           // four chunks' loads in flight per row
   for (int c = lane; c < cpr; c += 64) {
     const u32x4 xv = reinterpret_cast<const u32x4*>(x)[c];
     u32x4 wv[R];
@@ -557,10 +558,10 @@ void launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, in
 
 }  // namespace
 
-// Launch table (timed per shape on MI355X, 31B-like shapes streamed cold): rows of up to 6144
-// elements use the one-shot kernel. The fused gate|up (43008 x 5376) stages x in LDS after its
-// weight loads; q|k|v (6144 x 5376, one row per wave) and o (5376 x 4096, two rows per wave,
-// two steps) stage x first. Long rows (the down projection, K = 21504) use the loop kernel with
+// Launch table (timed per shape on MI355X, 31B-like shapes streamed cold, then A/B inside the
+// token stream): rows of up to 6144 elements use the one-shot kernel. The fused gate|up
+// (43008 x 5376) stages x in LDS after its weight loads; q|k|v (6144 x 5376) and o (5376 x 4096,
+// two steps) take one row per wave and stage x first. Long rows (the down projection, K = 21504) use the loop kernel with
 // four rows per wave and K split over two waves (two row groups per workgroup): inside the
 // token stream this beat splits of 1 and 4 and 2 or 8 rows per wave.
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
@@ -569,7 +570,7 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
   if (W.K >= 16384)
     launch_nvfp4_loop<4, 2>(W, x, y, stream);
   else if (cpr <= 128)
-    launch_nvfp4_oneshot<2, 1, 2, true, 4, true, 2>(W, x, y, stream);    // K <= 4096: two steps per row (x: 2 x 256 >= K/8)
+    launch_nvfp4_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, stream);    // K <= 4096: one row per wave, two steps (x: 2 x 256 >= K/8)
   else if (cpr <= 192 && W.N >= 16384)
     launch_nvfp4_oneshot<2, 1, 3, true, 8>(W, x, y, stream);             // fused gate|up 43008x5376
   else if (cpr <= 192)
@@ -626,7 +627,7 @@ hipError_t launch_gemv_nvfp4_glu(const attnq_nvfp4& W, const uint16_t* x, int ac
 
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  constexpr int R = 4;
+  constexpr int R = 2;
   const unsigned grid = (unsigned)((N + 4 * R - 1) / (4 * R));
   k_gemv_bf16<R><<<grid, 256, 0, stream>>>(W, x, y, N, K);
   return hipGetLastError();
