@@ -58,7 +58,7 @@ LOWRANK_RANK = 16
 # HBM traffic of one fused gate|up launch from the FETCH_SIZE / WRITE_SIZE passes recorded in
 # profiles/gemv_nvfp4_31b_token_traffic.md (FETCH scaled x1.9999, WRITE x1.0 by a 1 GiB copy).
 # Valid only for the kernel sources it was measured on: reported as null once they change.
-GATE_UP_TRAFFIC = {"sources_sha256_16": "0a8c9404f408bd48", "bytes": 130376961}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "d8edb390f97963be", "bytes": 130378070}
 
 
 def gemv_sources_hash() -> str:
@@ -558,7 +558,7 @@ def main():
         "ms_per_token_eager": round(eager_ms, 5),
         "bytes_per_token": bytes_step,
         "weight_bytes_per_token": model.weight_bytes_per_step(),
-        "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4_oneshot<2,1,3,true,8,false,1,0> (fused gate|up 43008x5376)",
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4_oneshot<2,1,3,true,8,true,2,0> (fused gate|up 43008x5376)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (GATE_UP_TRAFFIC["bytes"] if gemv_sources_hash() == GATE_UP_TRAFFIC["sources_sha256_16"]

@@ -548,20 +548,21 @@ void launch_lr_loop(const attnq_nvfp4& W, const uint16_t* x, float* y, const Low
                                                        nullptr, 0, lr);
 }
 
-// gate|up epilogue launches: one row pair per wave, F = N / 2 pairs
+// gate|up epilogue launches: one row pair per wave, F = N / 2 pairs, x loaded ahead of the weights
 template <int S>
 void launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, int act, hipStream_t stream) {
   const unsigned grid = (unsigned)((W.N / 2 + 7) / 8);
-  k_gemv_nvfp4_oneshot<2, 1, S, true, 8, false, 1, 1><<<grid, 512, (size_t)W.K * 2, stream>>>(
+  k_gemv_nvfp4_oneshot<2, 1, S, true, 8, true, 2, 1><<<grid, 512, (size_t)W.K * 2, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, nullptr, W.N, W.K, h, act);
 }
 
 }  // namespace
 
 // Launch table (timed per shape on MI355X, 31B-like shapes streamed cold, then A/B inside the
-// token stream): rows of up to 6144 elements use the one-shot kernel. The fused gate|up
-// (43008 x 5376) stages x in LDS after its weight loads; q|k|v (6144 x 5376) and o (5376 x 4096,
-// two steps) take one row per wave and stage x first. Long rows (the down projection, K = 21504) use the loop kernel with
+// token stream): rows of up to 6144 elements use the one-shot kernel, with x loaded ahead of the
+// weights (in the stream each layer's x is cold, and loaded after the weights its latency would
+// add to theirs): the fused gate|up (43008 x 5376) with two rows per wave, q|k|v (6144 x 5376)
+// and o (5376 x 4096, two steps) with one. Long rows (the down projection, K = 21504) use the loop kernel with
 // four rows per wave and K split over two waves (two row groups per workgroup): inside the
 // token stream this beat splits of 1 and 4 and 2 or 8 rows per wave.
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
@@ -572,7 +573,7 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
   else if (cpr <= 128)
     launch_nvfp4_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, stream);    // K <= 4096: one row per wave, two steps (x: 2 x 256 >= K/8)
   else if (cpr <= 192 && W.N >= 16384)
-    launch_nvfp4_oneshot<2, 1, 3, true, 8>(W, x, y, stream);             // fused gate|up 43008x5376
+    launch_nvfp4_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused gate|up 43008x5376 (x: 2 x 512 >= K/8)
   else if (cpr <= 192)
     launch_nvfp4_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 2 x 512 >= K/8)
   else
@@ -599,9 +600,9 @@ hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, co
   if (W.K >= 16384)
     launch_lr_loop<4, 2>(W, x, y, lr, stream);
   else if (cpr <= 128)
-    launch_lr_oneshot<2, 1, 2, true, 4, true, 2>(W, x, y, lr, stream);
+    launch_lr_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, lr, stream);
   else if (cpr <= 192 && W.N >= 16384)
-    launch_lr_oneshot<2, 1, 3, true, 8>(W, x, y, lr, stream);
+    launch_lr_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
   else if (cpr <= 192)
     launch_lr_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
   else
