@@ -5,7 +5,9 @@
   set per segment);
 * activations at extreme magnitudes (2^100, -2^100 and 2^-100 next to ordinary values) and with
   exact zeros and a negative zero, where fp32 accumulation must neither overflow nor lose the large terms;
-* the smallest gate|up (F = 1) and a one-row weight in the small-M product.
+* the smallest gate|up (F = 1) and a one-row weight in the small-M product;
+* non-finite activations (+inf, NaN) in the GEMV and both small-M kernels: the NaN / +-inf
+  pattern of every output equals the float64 oracle's, and other tokens are unaffected.
 """
 import numpy as np
 import pytest
@@ -132,3 +134,54 @@ def test_glu_single_pair(A):
         a = O.activation(g, act)
         bound = 2.0 ** -8 * np.abs(href) + 2.0 ** -14 * (ad_g * np.abs(u) + ad_u * np.abs(a)) + 1e-30
         assert np.all(np.abs(hg - href) <= bound), (act, hg, href, bound)
+
+
+def _check_nonfinite(got, want, what):
+    """Non-finite outputs must sit where the oracle's are, with the same kind and sign."""
+    got = got.astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(want)), f"{what}: NaN pattern differs"
+    inf_w = np.isinf(want)
+    assert np.array_equal(np.isinf(got), inf_w), f"{what}: inf pattern differs"
+    assert np.array_equal(np.sign(got[inf_w]), np.sign(want[inf_w])), f"{what}: inf sign differs"
+
+
+@pytest.mark.filterwarnings("ignore:invalid value encountered")   # the oracle's inf * 0, by design
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_nonfinite_activations_propagate(A, M):
+    """x holding +inf at one position gives, row by row, NaN where the dequantized weight at that
+    position is zero (inf * 0) and +-inf elsewhere, exactly as the float64 oracle; a NaN anywhere
+    in x makes every output of that token NaN. Other tokens of a small-M product are unaffected."""
+    K = 1152
+    segs = (300, 41)
+    what = f"non-finite x, M {M}"
+    say(what)
+    b = _bundles(segs, K, 95)
+    W, seg_end = gpu_quantize(A, b, K)
+    c, s, t, _ = oracle_quantize(b)
+    X = inputs.activation_bf16(M, K, 9, 95, M).copy()
+    pinf, nan = inputs.bits_from_floats([float("inf")])[0], 0x7FC0
+    X[0, 5] = pinf
+    if M > 1:
+        X[1, K - 1] = nan
+    if M == 1:
+        y = torch.full((W.N,), 0.0, dtype=torch.float32, device="cuda")
+        A.attnq_gemv_nvfp4(W, dev(X.reshape(-1)), y)
+        torch.cuda.synchronize()
+        got = host(y)[None]
+        want = O.gemv_nvfp4(c, s, t, X, seg_end)[None]
+    else:
+        Y = torch.full((M, W.N), 0.0, dtype=torch.float32, device="cuda")
+        A.attnq_gemm_nvfp4_small_m(W, dev(X), Y)
+        torch.cuda.synchronize()
+        got = host(Y)
+        want = O.gemm_nvfp4_small_m(c, s, t, X, seg_end)
+    assert np.isnan(want[0]).any() and np.isinf(want[0]).any(), "the case must hold both kinds"
+    for m in range(M):
+        _check_nonfinite(got[m], want[m], f"{what} token {m}")
+    if M > 1:
+        assert np.all(np.isnan(got[1]))
+    # tokens without a non-finite input stay finite and within the GEMV bound
+    if M > 2:
+        ad = O.abs_dot(c, s, t, X, seg_end)
+        for m in range(2, M):
+            assert_close_products(got[m], want[m], ad[m], f"{what} finite token {m}")
