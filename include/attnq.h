@@ -186,8 +186,9 @@ ATTNQ_API attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, 
 
 /* Y[m][n] = sum_k X[m][k] * weight[n][k] for 0 <= M <= 16 token rows (speculative verify at
  * gamma + 1 = 4, batch 8). X row m at X + m*ldx (bf16, ldx >= K, ldx % 8 == 0, X 16-byte
- * aligned); Y row m at Y + m*ldy (fp32, ldy >= N, Y 4-byte aligned). Uses MFMA matrix cores;
- * fp32 accumulation. */
+ * aligned, (M - 1)*ldx + K < 2^30); Y row m at Y + m*ldy (fp32, ldy >= N, Y 4-byte aligned).
+ * Uses MFMA matrix cores; fp32 accumulation. Errors: as attnq_gemv_nvfp4; M outside [0, 16] or
+ * a stride or extent out of range is ATTNQ_ERR_SHAPE. */
 ATTNQ_API attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, int32_t M,
                                       int32_t ldx, float* Y, int32_t ldy, attnq_stream stream);
 

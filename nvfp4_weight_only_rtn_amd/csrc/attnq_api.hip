@@ -118,6 +118,8 @@ attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, i
   attnq_status st = check_nvfp4(W);
   if (st != ATTNQ_OK) return st;
   if (M < 0 || M > kMaxM || ldx < W->K || ldx % 8 != 0 || ldy < W->N) return ATTNQ_ERR_SHAPE;
+  // X is addressed with 32-bit byte offsets inside the kernels: its extent must stay below 2^30 elements
+  if (M > 0 && (int64_t)(M - 1) * ldx + W->K >= (int64_t{1} << 30)) return ATTNQ_ERR_SHAPE;
   if ((X == nullptr || Y == nullptr) && M != 0 && W->N != 0) return ATTNQ_ERR_NULL;
   if (!aligned(X, 16) || !aligned(Y, 4)) return ATTNQ_ERR_ALIGN;
   return from_hip(attnq::launch_gemm_nvfp4_small_m(*W, X, M, ldx, Y, ldy, static_cast<hipStream_t>(stream)));

@@ -174,4 +174,5 @@ def test_gemv_and_gemm_validation():
     assert g(ctypes.byref(nv), FAKE, 4, 32, FAKE, 64, None) == 2                  # ldx < K
     assert g(ctypes.byref(nv), FAKE, 4, 68, FAKE, 64, None) == 2                  # ldx % 8
     assert g(ctypes.byref(nv), FAKE, 4, 64, FAKE, 32, None) == 2                  # ldy < N
+    assert g(ctypes.byref(nv), FAKE, 4, 1 << 29, FAKE, 64, None) == 2             # X extent 3 * 2^29 + K >= 2^30
     assert g(ctypes.byref(nv), None, 4, 64, FAKE, 64, None) == 1
