@@ -256,9 +256,13 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 // One-shot variant for rows of at most S*64 chunks per wave slice: every wave issues the code
 // and scale loads of its whole slice (S steps x R rows) before computing, which keeps the most
 // bytes in flight per wave. With XL the workgroup stages x in LDS once, transposed so that the
-// four 16-byte quarter reads of a chunk ([q][chunk]) are each bank-conflict free. XFIRST issues
-// the x loads (at most XI 16-byte pieces per thread) before the weight loads, so the LDS staging
-// waits for x only; otherwise x is loaded after the weights (better for the tall gate|up shape).
+// four 16-byte quarter reads of a chunk ([q][chunk]) are each bank-conflict free. XFIRST loads x
+// (at most XI 16-byte pieces per thread) into registers ahead of the weight loads; without it, x
+// is loaded after them in a plain loop. The LDS store of a piece is guarded (pieces past x are
+// skipped), and the compiler moves the load of a thread's first piece into that guarded store,
+// behind the weight loads, so the staging waits for all of the wave's loads. A branch-free store
+// that keeps every x load first, so that the staging waits for x alone, measured slower inside
+// the token stream.
 template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1, int EPI = 0>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t* __restrict__ codes,
                                                                    const uint8_t* __restrict__ scales,
@@ -559,12 +563,13 @@ void launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, in
 }  // namespace
 
 // Launch table (timed per shape on MI355X, 31B-like shapes streamed cold, then A/B inside the
-// token stream): rows of up to 6144 elements use the one-shot kernel, with x loaded ahead of the
-// weights (in the stream each layer's x is cold, and loaded after the weights its latency would
-// add to theirs): the fused gate|up (43008 x 5376) with two rows per wave, q|k|v (6144 x 5376)
-// and o (5376 x 4096, two steps) with one. Long rows (the down projection, K = 21504) use the loop kernel with
-// four rows per wave and K split over two waves (two row groups per workgroup): inside the
-// token stream this beat splits of 1 and 4 and 2 or 8 rows per wave.
+// token stream): rows of up to 6144 elements use the one-shot kernel with x loaded ahead of the
+// weights (XFIRST: better inside the stream, where each layer's x is cold): the fused gate|up
+// (43008 x 5376) with two rows per wave, q|k|v (6144 x 5376) and o (5376 x 4096, two steps) with
+// one. Long rows (the down projection, K = 21504) use the loop kernel with four rows per wave and
+// K split over two waves (two row groups per workgroup): inside the token stream this beat
+// splits of 1 and 4, 2 or 8 rows per wave, x staged in LDS, the one-shot kernel and a balanced
+// walk with one workgroup per compute unit.
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
   if (W.N == 0) return hipSuccess;
   const int cpr = W.K / 32;

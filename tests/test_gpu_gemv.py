@@ -69,6 +69,34 @@ def test_gemv_long_rows_segments(A, segs):
     _gemv_case(A, bs, K, x, f"gemv long rows {segs}x{K}")
 
 
+# more long-row shapes for the K-split loop kernel: row counts near 1800 (a ragged last workgroup),
+# K = 16384, 16416 (a ragged last step in each K half) and 24576, three- and two-segment weights
+# whose boundaries fall inside a workgroup's rows
+@pytest.mark.parametrize("segs,K", [((1792,), 16384), ((700, 3, 1097), 16416), ((1000, 799), 24576)])
+def test_gemv_long_rows_more_shapes(A, segs, K):
+    bs = [inputs.theta_bundle(n, K, 0, cfg=9, layer=35, proj=i, passthrough=True) for i, n in enumerate(segs)]
+    x = inputs.activation_bf16(1, K, 9, 35, len(segs))
+    _gemv_case(A, bs, K, x, f"gemv long rows {segs}x{K}")
+
+
+def test_gemv_one_hot_columns_are_exact_long_rows(A):
+    """One-hot x through the K-split loop kernel: the other K half's partial sum is zero, so the
+    fp32 dequantized column comes back bit for bit."""
+    N, K = 1800, 16416
+    b = inputs.theta_bundle(N, K, 0, cfg=9, layer=36, proj=0, passthrough=True)
+    say("one-hot gemv, long rows")
+    W, _ = gpu_quantize(A, [b], K)
+    c, s, t, _ = oracle_quantize([b])
+    deq32 = O.dequantize_f32(c, s, t)
+    y = torch.empty((N,), dtype=torch.float32, device="cuda")
+    for k in (0, 31, 2048, 8209, K - 1):
+        xb = np.zeros(K, np.uint16)
+        xb[k] = 0x3F80
+        A.attnq_gemv_nvfp4(W, dev(xb), y)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), deq32[:, k]), k
+
+
 def test_gemv_one_hot_columns_are_exact(A):
     N, K = 96, 2048
     b = inputs.theta_bundle(N, K, 0, cfg=9, layer=31, proj=0, passthrough=True)
