@@ -84,6 +84,8 @@ typedef struct attnq_theta {
  *   tensor_scale [n_seg] fp32, 4-byte aligned: the dequantization multiplier of a segment.
  *   weight[n][k] = e2m1(code) * e4m3(scale[n][k/16]) * tensor_scale[segment of n].
  *   1 <= n_seg <= 4, seg_end strictly ascending, seg_end[n_seg-1] == N.
+ *   N * K/2 <= 2^32: the kernels address codes and scales with 32-bit byte offsets (every call
+ *   that takes an attnq_nvfp4 returns ATTNQ_ERR_SHAPE beyond that).
  *   layout: ATTNQ_LAYOUT_ROW_MAJOR (0) is the only layout. */
 typedef struct attnq_nvfp4 {
   uint8_t* codes;

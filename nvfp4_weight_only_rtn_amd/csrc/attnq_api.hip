@@ -31,6 +31,8 @@ attnq_status check_nvfp4(const attnq_nvfp4* w) {
   if ((w->codes == nullptr || w->scales == nullptr) && w->N != 0) return ATTNQ_ERR_NULL;
   if (w->layout != ATTNQ_LAYOUT_ROW_MAJOR) return ATTNQ_ERR_LAYOUT;
   if (w->N < 0 || w->K <= 0 || w->K % 32 != 0) return ATTNQ_ERR_SHAPE;
+  // codes and scales are addressed with 32-bit byte offsets inside the kernels
+  if ((int64_t)w->N * (w->K / 2) > (int64_t{1} << 32)) return ATTNQ_ERR_SHAPE;
   if (w->n_seg < 1 || w->n_seg > ATTNQ_MAX_SEGMENTS) return ATTNQ_ERR_SEGMENT;
   int32_t prev = 0;
   for (int i = 0; i < w->n_seg; ++i) {

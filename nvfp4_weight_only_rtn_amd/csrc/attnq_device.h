@@ -76,15 +76,35 @@ __device__ __forceinline__ float tensor_scale_from_amax_bits(uint32_t bits) {
   return __uint_as_float(bits) / kTsDivisor;
 }
 
-// Sum over the 64 lanes of a wave; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+// v from the lane CTRL selects (DPP), 0 where the row mask excludes a row or the source lane
+// does not exist
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sums over the 64 lanes of a wave of n values at once; every lane receives the totals. Inside
+// each row of 16 lanes, shifts by 1, 2, 4 and 8 leave the row's sum in its last lane;
+// row_bcast:15 adds row 0's sum into row 1 and row 2's into row 3, and row_bcast:31 adds lane
+// 31's into rows 2 and 3, so lane 63 ends with the total, which is read into a scalar register
+// (no LDS round trip). The values advance step by step together, so that independent DPP
+// operations fill each other's wait states. All 64 lanes must be active.
+template <int n>
+__device__ __forceinline__ void wave_sums(float* v) {
+#pragma unroll
+  for (int i = 0; i < n; ++i) v[i] += dpp_f32<0x111, 0xF>(v[i]);
+#pragma unroll
+  for (int i = 0; i < n; ++i) v[i] += dpp_f32<0x112, 0xF>(v[i]);
+#pragma unroll
+  for (int i = 0; i < n; ++i) v[i] += dpp_f32<0x114, 0xF>(v[i]);
+#pragma unroll
+  for (int i = 0; i < n; ++i) v[i] += dpp_f32<0x118, 0xF>(v[i]);
+#pragma unroll
+  for (int i = 0; i < n; ++i) v[i] += dpp_f32<0x142, 0xA>(v[i]);
+#pragma unroll
+  for (int i = 0; i < n; ++i) v[i] += dpp_f32<0x143, 0xC>(v[i]);
+#pragma unroll
+  for (int i = 0; i < n; ++i) v[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[i]), 63));
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -134,7 +134,8 @@ __device__ __forceinline__ void lr_row_terms(const LrRegs<R, PF>& st, const LowR
     const uint16_t* u = lr.U + (size_t)row * lr.r;
     const int g = segment_of(segs, row);
     const float* pg = lr.part + (size_t)g * n;
-    float c = 0.0f;
+    float& c = d[r];
+    c = 0.0f;
     if (n > 0) {
       if (PF > 0 && g == st.g0 && 64 % lr.r == 0) {
         const float uk = bf16_bits_to_f32((uint16_t)st.ub[r]);
@@ -146,8 +147,8 @@ __device__ __forceinline__ void lr_row_terms(const LrRegs<R, PF>& st, const LowR
         for (int i = lane + 64 * ks; i < n; i += 64 * KS) c = __builtin_fmaf(bf16_bits_to_f32(u[i % lr.r]), pg[i], c);
       }
     }
-    d[r] = wave_sum(c);
   }
+  wave_sums<R>(d);
 }
 
 __device__ __forceinline__ float lr_finish(float v, float ts, const LowRank& lr, uint32_t s_bits, float d) {
@@ -183,8 +184,16 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 
+  // 32-bit byte offsets from the (uniform) tensor bases, one row offset per row
+  uint32_t crow[R], srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t row = (uint32_t)row_of(r);        // clamp: rows past N load row N-1, result discarded
+    crow[r] = row * (uint32_t)code_pitch;
+    srow[r] = row * (uint32_t)scale_pitch;
+  }
   for (int c = c_begin + lane; c < c_end; c += 64) {
-    const u32x4* xp = reinterpret_cast<const u32x4*>(x + (size_t)c * kChunkElems);
+    const u32x4* xp = reinterpret_cast<const u32x4*>(x) + 4u * (uint32_t)c;
     const u32x4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
     const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
                              x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
@@ -192,9 +201,8 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
     uint32_t sv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = row_of(r);                     // clamp: rows past N load row N-1, result discarded
-      cv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + row * code_pitch) + c);
-      sv[r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
+      cv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + (crow[r] + 16u * (uint32_t)c)));
+      sv[r] = *reinterpret_cast<const uint16_t*>(scales + (srow[r] + 2u * (uint32_t)c));
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = chunk_dot(cv[r], sv[r], xw, acc[r]);
@@ -204,8 +212,7 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
   // across the loop would cost the stream occupancy)
   [[maybe_unused]] LrRegs<R, 4> lrs;
   if constexpr (EPI == 2) lr_prefetch<R, 4, KSPLIT>(lrs, lr, segs, row_of, lane, ks, x);
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  wave_sums<R>(acc);
   [[maybe_unused]] float lrd = 0.0f;
   if constexpr (EPI == 2) {
     float d[R];
@@ -273,7 +280,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   static_assert(WAVES % KSPLIT == 0, "K split must divide the waves of a workgroup");
   static_assert(!XFIRST || XL, "x-first staging is an LDS staging");
   static_assert(EPI != 1 || (R == 2 && KSPLIT == 1), "the gate|up epilogue takes one row pair per wave");
-  extern __shared__ u32x4 xs[];
+  // x in LDS as [quarter][chunk] with a compile-time pitch (the longest row the kernel takes,
+  // KSPLIT x S x 64 chunks), so the four quarter reads of a chunk use immediate offsets
+  constexpr int kPitch = KSPLIT * S * 64;
+  __shared__ u32x4 xs[XL ? 4 * kPitch : 1];
   constexpr int kRowGroups = WAVES / KSPLIT;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -294,16 +304,24 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
 #pragma unroll
     for (int j = 0; j < XI; ++j) xst[j] = xg[min((int)threadIdx.x + j * 64 * WAVES, K / 8 - 1)];
   }
+  // 32-bit byte offsets from the (uniform) tensor bases: one row offset per row, and each load
+  // adds only its (clamped) chunk offset
+  uint32_t crow[R], srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t row = (uint32_t)row_of(r);
+    crow[r] = row * (uint32_t)(K >> 1);
+    srow[r] = row * (uint32_t)(K >> 4);
+  }
   u32x4 cv[S][R];
   uint32_t sv[S][R];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const int c = min(c_begin + s * 64 + lane, cpr - 1);       // clamped: lanes past the slice reload a valid chunk
+    const uint32_t c = (uint32_t)min(c_begin + s * 64 + lane, cpr - 1);   // clamped: lanes past the slice reload a valid chunk
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = row_of(r);
-      cv[s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + row * code_pitch) + c);
-      sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + row * scale_pitch + 2 * c);
+      cv[s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + (crow[r] + 16u * c)));
+      sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + (srow[r] + 2u * c));
     }
   }
   [[maybe_unused]] LrRegs<R, 2> lrs;
@@ -312,11 +330,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
       const int i = threadIdx.x + j * 64 * WAVES;
-      if (i < K / 8) xs[(i & 3) * cpr + (i >> 2)] = xst[j];
+      if (i < K / 8) xs[(i & 3) * kPitch + (i >> 2)] = xst[j];
     }
     __syncthreads();
   } else if constexpr (XL) {
-    for (int i = threadIdx.x; i < K / 8; i += 64 * WAVES) xs[(i & 3) * cpr + (i >> 2)] = xg[i];
+    for (int i = threadIdx.x; i < K / 8; i += 64 * WAVES) xs[(i & 3) * kPitch + (i >> 2)] = xg[i];
     __syncthreads();
   }
   float acc[R];
@@ -328,7 +346,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
     if (c < c_end) {
       u32x4 x0, x1, x2, x3;
       if constexpr (XL) {
-        x0 = xs[c]; x1 = xs[cpr + c]; x2 = xs[2 * cpr + c]; x3 = xs[3 * cpr + c];
+        x0 = xs[c]; x1 = xs[kPitch + c]; x2 = xs[2 * kPitch + c]; x3 = xs[3 * kPitch + c];
       } else {
         const u32x4* xp = reinterpret_cast<const u32x4*>(x + (size_t)c * kChunkElems);
         x0 = xp[0]; x1 = xp[1]; x2 = xp[2]; x3 = xp[3];
@@ -339,8 +357,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
       for (int r = 0; r < R; ++r) acc[r] = chunk_dot(cv[s][r], sv[s][r], xw, acc[r]);
     }
   }
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  wave_sums<R>(acc);
   [[maybe_unused]] float lrd = 0.0f;
   if constexpr (EPI == 2) {
     float d[R];
@@ -417,8 +434,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
       acc[r] = a;
     }
   }
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  wave_sums<R>(acc);
   if (lane < R) {
     float v = acc[0];
 #pragma unroll
@@ -521,13 +537,16 @@ void launch_nvfp4_loop(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStr
   k_gemv_nvfp4<R, KSPLIT><<<grid, 256, 0, stream>>>(W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
 }
 
+// The one-shot launchers refuse (launch nothing, return false) rows longer than the kernel's
+// KSPLIT x S x 64 chunks, which is also the pitch of its x staging in LDS.
 template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1>
-void launch_nvfp4_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
+bool launch_nvfp4_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
+  if (W.K / 32 > KSPLIT * S * 64) return false;
   constexpr int rows_per_wg = R * (WAVES / KSPLIT);
   const unsigned grid = (unsigned)((W.N + rows_per_wg - 1) / rows_per_wg);
-  const size_t lds = XL ? (size_t)W.K * 2 : 0;
-  k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI><<<grid, 64 * WAVES, lds, stream>>>(
+  k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI><<<grid, 64 * WAVES, 0, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K);
+  return true;
 }
 
 int lowrank_parts(int K, int r) {
@@ -536,12 +555,13 @@ int lowrank_parts(int K, int r) {
 }
 
 template <int R, int KSPLIT, int S, bool XL, int WAVES, bool XFIRST = false, int XI = 1>
-void launch_lr_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, const LowRank& lr, hipStream_t stream) {
+bool launch_lr_oneshot(const attnq_nvfp4& W, const uint16_t* x, float* y, const LowRank& lr, hipStream_t stream) {
+  if (W.K / 32 > KSPLIT * S * 64) return false;
   constexpr int rows_per_wg = R * (WAVES / KSPLIT);
   const unsigned grid = (unsigned)((W.N + rows_per_wg - 1) / rows_per_wg);
-  const size_t lds = XL ? (size_t)W.K * 2 : 0;
-  k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI, 2><<<grid, 64 * WAVES, lds, stream>>>(
+  k_gemv_nvfp4_oneshot<R, KSPLIT, S, XL, WAVES, XFIRST, XI, 2><<<grid, 64 * WAVES, 0, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K, nullptr, 0, lr);
+  return true;
 }
 
 template <int R, int KSPLIT>
@@ -554,10 +574,12 @@ void launch_lr_loop(const attnq_nvfp4& W, const uint16_t* x, float* y, const Low
 
 // gate|up epilogue launches: one row pair per wave, F = N / 2 pairs, x loaded ahead of the weights
 template <int S>
-void launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, int act, hipStream_t stream) {
+bool launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, int act, hipStream_t stream) {
+  if (W.K / 32 > S * 64) return false;
   const unsigned grid = (unsigned)((W.N / 2 + 7) / 8);
-  k_gemv_nvfp4_oneshot<2, 1, S, true, 8, true, 2, 1><<<grid, 512, (size_t)W.K * 2, stream>>>(
+  k_gemv_nvfp4_oneshot<2, 1, S, true, 8, true, 2, 1><<<grid, 512, 0, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, nullptr, W.N, W.K, h, act);
+  return true;
 }
 
 }  // namespace
@@ -573,17 +595,18 @@ void launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, in
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
   if (W.N == 0) return hipSuccess;
   const int cpr = W.K / 32;
+  bool ok = true;
   if (W.K >= 16384)
     launch_nvfp4_loop<4, 2>(W, x, y, stream);
   else if (cpr <= 128)
-    launch_nvfp4_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, stream);    // K <= 4096: one row per wave, two steps (x: 2 x 256 >= K/8)
+    ok = launch_nvfp4_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, stream);    // K <= 4096: one row per wave, two steps (x: 2 x 256 >= K/8)
   else if (cpr <= 192 && W.N >= 16384)
-    launch_nvfp4_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused gate|up 43008x5376 (x: 2 x 512 >= K/8)
+    ok = launch_nvfp4_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused gate|up 43008x5376 (x: 2 x 512 >= K/8)
   else if (cpr <= 192)
-    launch_nvfp4_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 2 x 512 >= K/8)
+    ok = launch_nvfp4_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 2 x 512 >= K/8)
   else
     launch_nvfp4_loop<2, 2>(W, x, y, stream);
-  return hipGetLastError();
+  return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 // Runtime low-rank product over a shared NVFP4 block: the partial sums of t = V^T x (one
@@ -602,17 +625,18 @@ hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, co
     k_lowrank_part<<<dim3((unsigned)lr.P, (unsigned)W.n_seg), kLrThreads, 0, stream>>>(V, x, ws, W.K, r, lr.P);
   }
   const int cpr = W.K / 32;
+  bool ok = true;
   if (W.K >= 16384)
     launch_lr_loop<4, 2>(W, x, y, lr, stream);
   else if (cpr <= 128)
-    launch_lr_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, lr, stream);
+    ok = launch_lr_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, lr, stream);
   else if (cpr <= 192 && W.N >= 16384)
-    launch_lr_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
+    ok = launch_lr_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
   else if (cpr <= 192)
-    launch_lr_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
+    ok = launch_lr_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
   else
     launch_lr_loop<2, 2>(W, x, y, lr, stream);
-  return hipGetLastError();
+  return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 // gate|up with its activation: the one-shot kernel stages x in LDS for rows of up to 6144
@@ -620,15 +644,16 @@ hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, co
 hipError_t launch_gemv_nvfp4_glu(const attnq_nvfp4& W, const uint16_t* x, int act, uint16_t* h, hipStream_t stream) {
   if (W.N == 0) return hipSuccess;
   const int cpr = W.K / 32;
+  bool ok = true;
   if (cpr <= 64)
-    launch_glu_oneshot<1>(W, x, h, act, stream);
+    ok = launch_glu_oneshot<1>(W, x, h, act, stream);
   else if (cpr <= 128)
-    launch_glu_oneshot<2>(W, x, h, act, stream);
+    ok = launch_glu_oneshot<2>(W, x, h, act, stream);
   else if (cpr <= 192)
-    launch_glu_oneshot<3>(W, x, h, act, stream);
+    ok = launch_glu_oneshot<3>(W, x, h, act, stream);
   else
     launch_glu_loop(W, x, h, act, stream);
-  return hipGetLastError();
+  return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream) {

@@ -141,6 +141,10 @@ def test_gemv_and_gemm_validation():
     assert lib.attnq_gemv_nvfp4(ctypes.byref(nv), FAKE + 8, FAKE, None) == 3
     assert lib.attnq_gemv_nvfp4(ctypes.byref(nv), FAKE, FAKE + 2, None) == 3
     assert lib.attnq_gemv_nvfp4(ctypes.byref(_nv(K=16)), FAKE, FAKE, None) == 2
+    big = _nv(N=1 << 20, K=8192 + 64)                                             # N * K/2 > 2^32 code bytes
+    assert lib.attnq_gemv_nvfp4(ctypes.byref(big), FAKE, FAKE, None) == 2
+    assert lib.attnq_gemm_nvfp4_small_m(ctypes.byref(big), FAKE, 4, 8192 + 64, FAKE, 1 << 20, None) == 2
+    assert lib.attnq_quantize_nvfp4(ctypes.byref(_th(N=1 << 20, K=8192 + 64)), ctypes.byref(big), 0, None) == 2
     assert lib.attnq_gemv_bf16(FAKE, 10, 40, FAKE, FAKE, None) == 2
     assert lib.attnq_gemv_bf16(FAKE, -1, 64, FAKE, FAKE, None) == 2
     assert lib.attnq_gemv_bf16(None, 10, 64, FAKE, FAKE, None) == 1
