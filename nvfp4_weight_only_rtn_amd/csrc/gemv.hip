@@ -69,7 +69,7 @@ __device__ __forceinline__ void store_glu(uint16_t* h, int j, float g, float u, 
 
 // Runtime low-rank epilogue (EPI 2): for a row of segment g,
 //   y[row] = s[row] * (x . weight0[row]) + sum_k U[row][k] t[g][k],  t[g] = V[g]^T x.
-// k_lowrank_part leaves P partial sums of t per segment (one per 32 KB chunk of V), laid out
+// The partial-sum kernels leave P partial sums of t per segment (one per 32 KB chunk of V), laid out
 // part[g][p][k]. Each wave folds them into its rows directly: with n = P r, lane l takes the
 // flat indices i = l, l + 64, ... < n and sums U[row][i mod r] * part[g][i] (a fixed order), and
 // the wave adds its lanes. The one-shot kernels load a lane's first two values right after the
@@ -445,75 +445,132 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
 }
 
 // part[g][p][k] = sum over the rows j of chunk p of x[j] V[g][j][k] (V [n_seg][K][r] bf16), one
-// workgroup per (chunk, segment); a chunk is floor(16384 / r) rows of V. For r a power of two a
-// thread loads eight 16-byte pieces of the chunk (issued before x is staged), and its element i
-// always falls in column (8 tid + i) mod r, so it keeps eight column sums; the workgroup then
-// adds the slots of one column in a fixed tree. Other ranks take one column per thread.
-__global__ __launch_bounds__(kLrThreads) void k_lowrank_part(const uint16_t* __restrict__ V,
-                                                             const uint16_t* __restrict__ x, float* __restrict__ part,
-                                                             int K, int r, int P) {
+// workgroup per (chunk, segment); a chunk is floor(16384 / r) rows of V.
+//
+// r a power of two (k_lowrank_part_pow2): a thread loads eight 16-byte pieces of the chunk and,
+// with each, the aligned 8-element block of x that holds the piece's rows (x is not staged). Its
+// element i always falls in column (8 tid + i) mod r, so it keeps eight column sums; the threads
+// sharing a set of columns are those equal modulo c = max(1, r / 8). Each wave adds them within
+// rows of 16 lanes by DPP shifts of c, 2c, ... (the last c lanes of a row end with their class's
+// sums), one LDS slot per row and class takes those, and after a single barrier thread k < r
+// adds column k's 16 row slots in order.
+template <int C>
+__device__ __forceinline__ void class_row_sums(float* acc) {
+  // acc[i] of lane L gains lanes L - C, L - 2C, ... of its row of 16 (same class modulo C)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (C <= 1) acc[i] += dpp_f32<0x111, 0xF>(acc[i]);   // row_shr:1
+    if constexpr (C <= 2) acc[i] += dpp_f32<0x112, 0xF>(acc[i]);   // row_shr:2
+    if constexpr (C <= 4) acc[i] += dpp_f32<0x114, 0xF>(acc[i]);   // row_shr:4
+    acc[i] += dpp_f32<0x118, 0xF>(acc[i]);                         // row_shr:8
+  }
+}
+
+// element k (0..7) of 8 packed bf16, as fp32
+__device__ __forceinline__ float bf16_element(const u32x4& b, int k) {
+  const int d = k >> 1;
+  const uint32_t w = d == 0 ? b.x : d == 1 ? b.y : d == 2 ? b.z : b.w;
+  return __builtin_bit_cast(float, (k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+__global__ void k_lowrank_part_cols(const uint16_t* __restrict__ V, const uint16_t* __restrict__ x,
+                                    float* __restrict__ part, int K, int r, int P);
+
+template <int SH>
+__global__ __launch_bounds__(kLrThreads) void k_lowrank_part_pow2(const uint16_t* __restrict__ V,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  float* __restrict__ part, int K, int P) {
   constexpr int kRounds = kLrChunk / (kLrThreads * 8);
-  __shared__ float l1[kLrThreads * 8];
+  constexpr int r = 1 << SH, sh = SH;
+  __shared__ float slot[kLrThreads / 16][8][8];              // [row of 16 lanes][class][i]
+  const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int KC = kLrChunk >> sh, j0 = p * KC, rows = min(KC, K - j0);
+  const int E = rows << sh;                                   // rows and E are multiples of 32
+  const uint16_t* Vc = V + ((size_t)g * K + j0) * r;
+  const u32x4* xc = reinterpret_cast<const u32x4*>(x + j0);   // j0 is a multiple of 256
+  float* out = part + ((size_t)g * P + p) * r;
+  u32x4 v[kRounds], xb[kRounds];
+#pragma unroll
+  for (int m = 0; m < kRounds; ++m) {
+    const int e0 = (m * kLrThreads + tid) * 8;
+    const bool in = e0 < E;
+    v[m] = in ? *reinterpret_cast<const u32x4*>(Vc + e0) : u32x4{0u, 0u, 0u, 0u};
+    // rows (e0 >> sh) .. of this piece; zeros past the chunk, as for v (0 * 0 adds nothing, where
+    // a real x element could be infinite)
+    xb[m] = in ? xc[(e0 >> sh) >> 3] : u32x4{0u, 0u, 0u, 0u};
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int m = 0; m < kRounds; ++m) {
+    const int e0 = (m * kLrThreads + tid) * 8;                // lanes past E hold zeros in v
+    const int k0 = (e0 >> sh) & 7;
+    const uint32_t w[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float vi = __builtin_bit_cast(float, (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+      acc[i] = __builtin_fmaf(bf16_element(xb[m], k0 + (i >> sh)), vi, acc[i]);
+    }
+  }
+  constexpr int c = r >= 8 ? r >> 3 : 1;
+  class_row_sums<c>(acc);
+  const int L = tid & 15;
+  if (L >= 16 - c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) slot[tid >> 4][L - (16 - c)][i] = acc[i];
+  }
+  __syncthreads();
+  if (tid < r) {
+    float t = 0.0f;
+    if constexpr (r >= 8) {
+      for (int row = 0; row < kLrThreads / 16; ++row) t += slot[row][tid >> 3][tid & 7];
+    } else {
+      for (int row = 0; row < kLrThreads / 16; ++row)
+        for (int i = tid; i < 8; i += r) t += slot[row][0][i];
+    }
+    out[tid] = t;
+  }
+}
+
+void launch_lowrank_part(const uint16_t* V, const uint16_t* x, float* ws, int K, int r, int P, int n_seg,
+                         hipStream_t stream) {
+  const dim3 grid((unsigned)P, (unsigned)n_seg);
+  switch (r) {
+    case 1: k_lowrank_part_pow2<0><<<grid, kLrThreads, 0, stream>>>(V, x, ws, K, P); break;
+    case 2: k_lowrank_part_pow2<1><<<grid, kLrThreads, 0, stream>>>(V, x, ws, K, P); break;
+    case 4: k_lowrank_part_pow2<2><<<grid, kLrThreads, 0, stream>>>(V, x, ws, K, P); break;
+    case 8: k_lowrank_part_pow2<3><<<grid, kLrThreads, 0, stream>>>(V, x, ws, K, P); break;
+    case 16: k_lowrank_part_pow2<4><<<grid, kLrThreads, 0, stream>>>(V, x, ws, K, P); break;
+    case 32: k_lowrank_part_pow2<5><<<grid, kLrThreads, 0, stream>>>(V, x, ws, K, P); break;
+    case 64: k_lowrank_part_pow2<6><<<grid, kLrThreads, 0, stream>>>(V, x, ws, K, P); break;
+    default: k_lowrank_part_cols<<<grid, kLrThreads, 0, stream>>>(V, x, ws, K, r, P); break;
+  }
+}
+
+// Other ranks (k_lowrank_part_cols): x staged in LDS, one column per thread, the workgroup's
+// column slots added in order.
+__global__ __launch_bounds__(kLrThreads) void k_lowrank_part_cols(const uint16_t* __restrict__ V,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  float* __restrict__ part, int K, int r, int P) {
+  __shared__ float l1[kLrThreads];
   __shared__ uint16_t xl[kLrChunk];
   const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int KC = kLrChunk / r, j0 = p * KC, rows = min(KC, K - j0);
   const uint16_t* Vc = V + ((size_t)g * K + j0) * r;
   float* out = part + ((size_t)g * P + p) * r;
-  const bool pow2 = (r & (r - 1)) == 0;
-  const int E = rows * r;                                     // a multiple of 32 when r is a power of two
-  u32x4 v[kRounds];
-  if (pow2) {
-#pragma unroll
-    for (int m = 0; m < kRounds; ++m) {
-      const int e0 = (m * kLrThreads + tid) * 8;
-      v[m] = e0 < E ? *reinterpret_cast<const u32x4*>(Vc + e0) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
   for (int j = tid; j < rows; j += kLrThreads) xl[j] = x[j0 + j];
   __syncthreads();
-  if (pow2) {
-    const int sh = __builtin_ctz(r);
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < kRounds; ++m) {
-      const int e0 = (m * kLrThreads + tid) * 8;
-      if (e0 < E) {
-        const uint32_t w[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float vi = __builtin_bit_cast(float, (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
-          acc[i] = __builtin_fmaf(bf16_bits_to_f32(xl[(e0 + i) >> sh]), vi, acc[i]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) l1[tid * 8 + i] = acc[i];
-    __syncthreads();
-    float a = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) a += l1[tid + u * kLrThreads];   // slots of column tid mod r
-    __syncthreads();
-    l1[tid] = a;
-    __syncthreads();
-    if (tid < r) {
-      float t = 0.0f;
-      for (int q = 0; q < kLrThreads / r; ++q) t += l1[q * r + tid];
-      out[tid] = t;
-    }
-  } else {
-    const int G = kLrThreads / r, q = tid / r, k = tid - q * r;
-    float a = 0.0f;
-    if (q < G)
-      for (int j = q; j < rows; j += G) a = __builtin_fmaf(bf16_bits_to_f32(xl[j]), bf16_bits_to_f32(Vc[(size_t)j * r + k]), a);
-    l1[tid] = a;
-    __syncthreads();
-    if (tid < r) {
-      float t = 0.0f;
-      for (int qq = 0; qq < G; ++qq) t += l1[qq * r + tid];
-      out[tid] = t;
-    }
+  const int G = kLrThreads / r, q = tid / r, k = tid - q * r;
+  float a = 0.0f;
+  if (q < G)
+    for (int j = q; j < rows; j += G) a = __builtin_fmaf(bf16_bits_to_f32(xl[j]), bf16_bits_to_f32(Vc[(size_t)j * r + k]), a);
+  l1[tid] = a;
+  __syncthreads();
+  if (tid < r) {
+    float t = 0.0f;
+    for (int qq = 0; qq < G; ++qq) t += l1[qq * r + tid];
+    out[tid] = t;
   }
 }
 
@@ -622,7 +679,7 @@ hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, co
   LowRank lr{s, U, ws, r, 0};
   if (r > 0) {
     lr.P = lowrank_parts(W.K, r);
-    k_lowrank_part<<<dim3((unsigned)lr.P, (unsigned)W.n_seg), kLrThreads, 0, stream>>>(V, x, ws, W.K, r, lr.P);
+    launch_lowrank_part(V, x, ws, W.K, r, lr.P, W.n_seg, stream);
   }
   const int cpr = W.K / 32;
   bool ok = true;
