@@ -116,8 +116,8 @@ ATTNQ_API attnq_status attnq_reconstruct(const attnq_theta* theta, uint16_t* W_e
  * amax == 0 gives ts = 0 and all scales 0. A NaN/inf in the segment gives ts = NaN, every
  * scale 0x7F and every code byte 0.
  * theta->N must equal the segment's row count and theta->K == dst->K. The segment's
- * tensor_scale slot is used as the amax accumulator while the call runs (four kernels in
- * stream order); other segments of dst are untouched.
+ * tensor_scale slot is zeroed and then accumulates the tensor scale while the call runs (three
+ * kernels in stream order); other segments of dst are untouched.
  * Errors: as attnq_reconstruct, plus ATTNQ_ERR_SEGMENT for a bad seg or row count and
  * ATTNQ_ERR_LAYOUT for an unknown layout. */
 ATTNQ_API attnq_status attnq_quantize_nvfp4(const attnq_theta* theta, const attnq_nvfp4* dst, int32_t seg,

@@ -62,15 +62,15 @@ __device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t acc, float a, float b,
 // q0 = w*y, r = fma(-q0, d, w) (exact), q = fma(r, y, q0) is the correctly rounded quotient when
 // d and y are normal (Markstein's theorem); its sign is copied from w so that -0 stays -0. A block whose d is zero or subnormal falls back to
 // the exact division and the software rounding rule (e2m1_magnitude), as does 0/0 there.
-__device__ __forceinline__ void quantize_block(const uint32_t wp[kBlock / 2], uint32_t amax_bits, uint32_t packed[2],
+__device__ __forceinline__ void quantize_block(const uint32_t wp[kBlock / 2], uint32_t ts_bits, uint32_t packed[2],
                                                uint32_t& scale_code) {
-  const float ts = tensor_scale_from_amax_bits(amax_bits);
+  const float ts = __uint_as_float(ts_bits);
   const float six_ts = 6.0f * ts;
   uint32_t bmax = 0;
 #pragma unroll
   for (int i = 0; i < kBlock / 2; ++i) bmax = max(bmax, max(wp[i] & 0x7FFFu, (wp[i] >> 16) & 0x7FFFu));
   const float bamax = bf16_bits_to_f32(bmax);
-  const float sb = (amax_bits == 0u) ? 0.0f : bamax / six_ts;
+  const float sb = (ts_bits == 0u) ? 0.0f : bamax / six_ts;     // ts == 0 exactly when amax == 0
   const uint32_t S = e4m3_encode_nonneg(sb);
   const float d = e4m3_to_f32(S) * ts;
   scale_code = S;
@@ -152,16 +152,19 @@ __global__ void k_zero_slot(uint32_t* slot) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *slot = 0u;
 }
 
-// Workgroup max of per-thread |w| bit patterns, folded into the segment slot with atomicMax.
-// The max of bit patterns is order-free, hence deterministic; NaN patterns sort above +inf.
-__device__ __forceinline__ void fold_amax(uint32_t m, uint32_t* slot) {
+// Workgroup max of per-thread |w| bit patterns, turned into the workgroup's tensor scale
+// fl32(amax / 2688) (NaN for a non-finite amax) and folded into the segment slot with atomicMax
+// on its bit pattern. A correctly rounded division by a positive constant is monotone, so the
+// largest workgroup scale is the segment's; the max of bit patterns is order-free, hence
+// deterministic, and NaN sorts above every finite scale. The slot ends holding the tensor scale.
+__device__ __forceinline__ void fold_tensor_scale(uint32_t m, uint32_t* slot) {
   __shared__ uint32_t red[4];
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    if (m) atomicMax(slot, m);
+    if (m) atomicMax(slot, __float_as_uint(tensor_scale_from_amax_bits(m)));
   }
 }
 
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(256) void k_amax_r0(Theta t, uint32_t* slot, int64_
     rebuild_block_r0(t, row, col, wp);
     m = amax_bits_of(wp, m);
   }
-  fold_amax(m, slot);
+  fold_tensor_scale(m, slot);
 }
 
 __global__ __launch_bounds__(256) void k_quantize_r0(Theta t, const uint32_t* __restrict__ slot, uint8_t* __restrict__ codes,
@@ -183,10 +186,10 @@ __global__ __launch_bounds__(256) void k_quantize_r0(Theta t, const uint32_t* __
   if (b >= nblocks) return;
   const int bpr = t.K / kBlock;
   const int row = (int)(b / bpr), cb = (int)(b % bpr);
-  const uint32_t amax_bits = *slot;
+  const uint32_t ts_bits = *slot;
   u32x2* cdst = reinterpret_cast<u32x2*>(codes + (size_t)row * (t.K / 2) + cb * (kBlock / 2));
   uint8_t* sdst = scales + (size_t)row * bpr + cb;
-  if (amax_bits >= 0x7F800000u) {                   // non-finite segment: NaN scales, zero codes
+  if (ts_bits >= 0x7F800000u) {                     // non-finite segment (ts NaN): NaN scales, zero codes
     *cdst = u32x2{0u, 0u};
     *sdst = 0x7F;
     return;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(256) void k_quantize_r0(Theta t, const uint32_t* __
   uint32_t wp[kBlock / 2];
   rebuild_block_r0(t, row, cb * kBlock, wp);
   uint32_t packed[2], S;
-  quantize_block(wp, amax_bits, packed, S);
+  quantize_block(wp, ts_bits, packed, S);
   *cdst = u32x2{packed[0], packed[1]};
   *sdst = (uint8_t)S;
 }
@@ -257,10 +260,10 @@ __global__ __launch_bounds__(256) void k_lowrank_tile(Theta t, uint32_t* slot, u
   const int tile_r = blockIdx.x / tiles_c, tile_c = blockIdx.x % tiles_c;
   const int row0 = tile_r * kTileRows, col0 = tile_c * kTileCols;
 
-  uint32_t amax_bits = 0;
+  uint32_t ts_bits = 0;
   if (PASS == kPassQuantize) {
-    amax_bits = *slot;
-    if (amax_bits >= 0x7F800000u) {               // non-finite segment: NaN scales, zero codes
+    ts_bits = *slot;
+    if (ts_bits >= 0x7F800000u) {                 // non-finite segment (ts NaN): NaN scales, zero codes
       const int cb = threadIdx.x & 15, rg = threadIdx.x >> 4;
       const int col = col0 + cb * kBlock;
       for (int rr = 0; rr < kRowsPerThread; ++rr) {
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(256) void k_lowrank_tile(Theta t, uint32_t* slot, u
     } else if (PASS == kPassQuantize) {
       if (ok) {
         uint32_t packed[2], S;
-        quantize_block(wp, amax_bits, packed, S);
+        quantize_block(wp, ts_bits, packed, S);
         *reinterpret_cast<u32x2*>(codes + (size_t)rows[rr] * (t.K / 2) + col / 2) = u32x2{packed[0], packed[1]};
         scales[(size_t)rows[rr] * (t.K / kBlock) + col / kBlock] = (uint8_t)S;
       }
@@ -345,14 +348,7 @@ __global__ __launch_bounds__(256) void k_lowrank_tile(Theta t, uint32_t* slot, u
       }
     }
   }
-  if (PASS == kPassAmax) fold_amax(m, slot);
-}
-
-__global__ void k_finalize(uint32_t* slot) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    const float ts = tensor_scale_from_amax_bits(*slot);
-    *reinterpret_cast<float*>(slot) = ts;
-  }
+  if (PASS == kPassAmax) fold_tensor_scale(m, slot);
 }
 
 Theta to_theta(const attnq_theta& t) { return Theta{t.W0, t.s, t.U, t.V, t.N, t.K, t.r}; }
@@ -395,7 +391,6 @@ hipError_t launch_quantize(const attnq_theta& th, uint8_t* codes, uint8_t* scale
       launch_lowrank<kPassQuantize>(t, slot, codes, scales, nullptr, stream);
     }
   }
-  k_finalize<<<1, 64, 0, stream>>>(slot);
   return hipGetLastError();
 }
 
