@@ -424,6 +424,7 @@ int pick_ks(const attnq_nvfp4& W) { return max(1, min(12, W.K / kSuper)); }
 hipError_t launch_gemm_nvfp4_small_m(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
                                      hipStream_t stream) {
   if (W.N == 0 || M == 0) return hipSuccess;
+  if (launch_gemm_nvfp4_tokens(W, X, M, ldx, Y, ldy, stream)) return hipGetLastError();
   if (M <= 4)
     launch_mfma<2, 1>(W, X, M, ldx, Y, ldy, pick_ks(W), stream);
   else

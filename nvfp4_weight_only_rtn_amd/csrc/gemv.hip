@@ -404,6 +404,115 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   }
 }
 
+// Small-M product for M = 1 .. 4 tokens on the batch-1 walk (rows of at most S x 64 chunks): the
+// weight loads are the one-shot kernel's (each wave load instruction 1 KiB of one row, all of a
+// lane's loads issued at once), every token's x is staged in LDS as [token][quarter][chunk], and a
+// wave decodes the fp4 chunk of each of its R rows once and takes its dot products with all MT
+// tokens. Per block and token the arithmetic is the batch-1 kernel's (dot2 chain, then the E4M3
+// scale by one FMA, the tensor scale last), and the launch shapes are the batch-1 table's, so a
+// token's row equals the batch-1 GEMV of that token bit for bit, whatever M is.
+template <int MT, int R, int S, int WAVES, int XI>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_nvfp4_tokens(const uint8_t* __restrict__ codes,
+                                                                  const uint8_t* __restrict__ scales,
+                                                                  const float* __restrict__ tensor_scale,
+                                                                  SegTable segs, const uint16_t* __restrict__ X,
+                                                                  int ldx, float* __restrict__ Y, int ldy, int N,
+                                                                  int K) {
+  constexpr int kPitch = S * 64;
+  __shared__ u32x4 xs[MT][4 * kPitch];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wave) * R;
+  const int cpr = K >> 5;
+  const u32x4* xg = reinterpret_cast<const u32x4*>(X);
+  const int xrow = ldx >> 3;                       // 16-byte pieces per X row (ldx % 8 == 0)
+
+  u32x4 xst[MT][XI];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < XI; ++j) xst[m][j] = xg[m * xrow + min((int)threadIdx.x + j * 64 * WAVES, K / 8 - 1)];
+  uint32_t crow[R], srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t row = (uint32_t)min(row0 + r, N - 1);    // rows past N load row N-1, result discarded
+    crow[r] = row * (uint32_t)(K >> 1);
+    srow[r] = row * (uint32_t)(K >> 4);
+  }
+  u32x4 cv[S][R];
+  uint32_t sv[S][R];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint32_t c = (uint32_t)min(s * 64 + lane, cpr - 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      cv[s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + (crow[r] + 16u * c)));
+      sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + (srow[r] + 2u * c));
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+      const int i = threadIdx.x + j * 64 * WAVES;
+      if (i < K / 8) xs[m][(i & 3) * kPitch + (i >> 2)] = xst[m][j];
+    }
+  __syncthreads();
+
+  float acc[R * MT];
+#pragma unroll
+  for (int a = 0; a < R * MT; ++a) acc[a] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = s * 64 + lane;
+    if (c < cpr) {
+      uint32_t wd[R][16];                            // the chunk of each row, decoded to bf16 pairs
+      float s0[R], s1[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t cw[4] = {cv[s][r].x, cv[s][r].y, cv[s][r].z, cv[s][r].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          wd[r][4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[d], 1.0f, 0));
+          wd[r][4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[d], 1.0f, 1));
+          wd[r][4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[d], 1.0f, 2));
+          wd[r][4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[d], 1.0f, 3));
+        }
+        s0[r] = __builtin_amdgcn_cvt_f32_fp8((int)sv[s][r], 0);
+        s1[r] = __builtin_amdgcn_cvt_f32_fp8((int)sv[s][r], 1);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4 x0 = xs[m][c], x1 = xs[m][kPitch + c], x2 = xs[m][2 * kPitch + c], x3 = xs[m][3 * kPitch + c];
+        const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                 x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            p0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wd[r][q]), as_bf16x2(xw[q]), p0, false);
+            p1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wd[r][8 + q]), as_bf16x2(xw[8 + q]), p1, false);
+          }
+          float a = acc[r * MT + m];
+          a = __builtin_fmaf(p0, s0[r], a);
+          a = __builtin_fmaf(p1, s1[r], a);
+          acc[r * MT + m] = a;
+        }
+      }
+    }
+  }
+  wave_sums<R * MT>(acc);
+  if (lane < R * MT) {
+    float v = acc[0];
+#pragma unroll
+    for (int a = 1; a < R * MT; ++a) v = (lane == a) ? acc[a] : v;
+    const int r = lane / MT, m = lane - r * MT;
+    const int row = row0 + r;
+    if (row < N) Y[(size_t)m * ldy + row] = v * tensor_scale[segment_of(segs, row)];
+  }
+}
+
 // bf16 weights: a lane owns one 16-byte chunk (8 bf16) of R rows per step; x chunk reused.
 template <int R>
 __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
@@ -666,6 +775,25 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
   return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
+// Small-M on the batch-1 walk: M = 1 .. 4 tokens and rows of at most 192 chunks, in the batch-1
+// launch shapes (o-like rows of up to 128 chunks: one row per wave, two steps, 4 waves; tall
+// weights: two rows per wave; otherwise one row per wave, 8 waves). Returns false (nothing
+// launched) for other shapes.
+template <int MT>
+void launch_tokens_mt(const attnq_nvfp4& W, const uint16_t* X, int ldx, float* Y, int ldy, hipStream_t stream) {
+  const int cpr = W.K / 32;
+  const SegTable t = seg_table(W);
+  if (cpr <= 128)          // x: 2 x 256 pieces >= K / 8
+    k_gemm_nvfp4_tokens<MT, 1, 2, 4, 2><<<(W.N + 3) / 4, 256, 0, stream>>>(W.codes, W.scales, W.tensor_scale, t, X,
+                                                                           ldx, Y, ldy, W.N, W.K);
+  else if (W.N >= 16384)   // x: 2 x 512 pieces >= K / 8
+    k_gemm_nvfp4_tokens<MT, 2, 3, 8, 2><<<(W.N + 15) / 16, 512, 0, stream>>>(W.codes, W.scales, W.tensor_scale, t,
+                                                                             X, ldx, Y, ldy, W.N, W.K);
+  else
+    k_gemm_nvfp4_tokens<MT, 1, 3, 8, 2><<<(W.N + 7) / 8, 512, 0, stream>>>(W.codes, W.scales, W.tensor_scale, t, X,
+                                                                           ldx, Y, ldy, W.N, W.K);
+}
+
 // Runtime low-rank product over a shared NVFP4 block: the partial sums of t = V^T x (one
 // workgroup per 16 KB chunk of V and segment), then the streaming GEMV with the s / U t epilogue,
 // in the same launch configurations as the plain GEMV.
@@ -711,6 +839,16 @@ hipError_t launch_gemv_nvfp4_glu(const attnq_nvfp4& W, const uint16_t* x, int ac
   else
     launch_glu_loop(W, x, h, act, stream);
   return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+bool launch_gemm_nvfp4_tokens(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
+                              hipStream_t stream) {
+  if (W.K / 32 > 192 || M < 1 || M > 4) return false;
+  if (M == 1) launch_tokens_mt<1>(W, X, ldx, Y, ldy, stream);
+  else if (M == 2) launch_tokens_mt<2>(W, X, ldx, Y, ldy, stream);
+  else if (M == 3) launch_tokens_mt<3>(W, X, ldx, Y, ldy, stream);
+  else launch_tokens_mt<4>(W, X, ldx, Y, ldy, stream);
+  return true;
 }
 
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream) {

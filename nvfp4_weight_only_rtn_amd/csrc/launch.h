@@ -19,5 +19,8 @@ int64_t lowrank_workspace_floats(int K, int n_seg, int r);
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_gemm_nvfp4_small_m(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
                                      hipStream_t stream);
+// M = 1 .. 4 on the batch-1 walk for rows of at most 192 chunks; false (nothing launched) otherwise
+bool launch_gemm_nvfp4_tokens(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
+                              hipStream_t stream);
 
 }  // namespace attnq

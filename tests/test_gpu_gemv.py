@@ -188,6 +188,25 @@ def test_small_m_ragged(A, N, K, M):
                           f"small-M ragged {M}x{N}x{K}")
 
 
+# rows of at most 192 chunks: M <= 4 runs on the batch-1 walk, and each token's row is the batch-1
+# GEMV of that token bit for bit (same launch shape, same per-block arithmetic and wave sums)
+@pytest.mark.parametrize("N,K", [(4097, 2080), (5376, 4096), (6144, 5376), (16400, 5376), (300, 96)])
+def test_small_m_tokens_equal_the_gemv_bitwise(A, N, K):
+    say(f"small-M vs GEMV bitwise {N}x{K}")
+    b = inputs.theta_bundle(N, K, 0, cfg=9, layer=37, proj=0, passthrough=True)
+    W, _ = gpu_quantize(A, [b], K)
+    X = inputs.activation_bf16(4, K, 9, 37, 1)
+    y = torch.empty((N,), dtype=torch.float32, device="cuda")
+    for M in (1, 2, 3, 4):
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        A.attnq_gemm_nvfp4_small_m(W, dev(X[:M]), Y)
+        torch.cuda.synchronize()
+        for m in range(M):
+            A.attnq_gemv_nvfp4(W, dev(X[m]), y)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(Y)[m].view(np.uint32), host(y).view(np.uint32)), (M, m)
+
+
 @pytest.mark.parametrize("M_small,M_big", [(1, 4), (2, 3), (5, 16), (8, 13)])
 def test_small_m_rows_are_independent_of_padding(A, M_small, M_big):
     """Token rows m < M must not depend on how many rows follow or what they hold: within one
