@@ -1,6 +1,10 @@
 // Small-M NVFP4 product Y = X * W^T for M <= 16 token rows: speculative verification of
 // gamma = 3 drafted tokens plus one ("Throughput", "Speculative decoding") and batch 8.
 //
+// M <= 4 with rows of at most 192 chunks (6144 elements) goes to the batch-1 walk first
+// (k_gemm_nvfp4_tokens, next to the GEMV kernels), which measured faster there; the matrix-core
+// kernels below take longer rows and M > 4.
+//
 // Matrix-core path, v_mfma_f32_16x16x32_bf16. Operand layout for lane l = 16 g + i (checked on
 // gfx950): A[i][8 g + e], B[8 g + e][i] for e = 0..7, and D[4 g + v][i] for v = 0..3.
 //
