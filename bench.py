@@ -58,7 +58,7 @@ LOWRANK_RANK = 16
 # HBM traffic of one fused gate|up launch from the FETCH_SIZE / WRITE_SIZE passes recorded in
 # profiles/gemv_nvfp4_31b_token_traffic.md (FETCH scaled x1.9999, WRITE x1.0 by a 1 GiB copy).
 # Valid only for the kernel sources it was measured on: reported as null once they change.
-GATE_UP_TRAFFIC = {"sources_sha256_16": "45c7318ca03668d5", "bytes": 130367848}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "d0d74530d64fcf9a", "bytes": 130371589}
 
 
 def gemv_sources_hash() -> str:
