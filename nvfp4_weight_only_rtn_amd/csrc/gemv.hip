@@ -208,8 +208,8 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
     for (int r = 0; r < R; ++r) acc[r] = chunk_dot(cv[r], sv[r], xw, acc[r]);
   }
 
-  // long rows: the low-rank operands are loaded after the main loop, all at once (holding them
-  // across the loop would cost the stream occupancy)
+  // long rows: the low-rank operands are loaded after the main loop, all at once (issued before
+  // the loop instead, their latency hidden, the low-rank stream measured the same)
   [[maybe_unused]] LrRegs<R, 4> lrs;
   if constexpr (EPI == 2) lr_prefetch<R, 4, KSPLIT>(lrs, lr, segs, row_of, lane, ks, x);
   wave_sums<R>(acc);
