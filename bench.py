@@ -57,15 +57,21 @@ LOWRANK_RANK = 16
 
 # HBM traffic of one fused gate|up launch from the FETCH_SIZE / WRITE_SIZE passes recorded in
 # profiles/gemv_nvfp4_31b_token_traffic.md (FETCH scaled x1.9999, WRITE x1.0 by a 1 GiB copy).
-# Valid only for the kernel sources it was measured on: reported as null once they change.
-GATE_UP_TRAFFIC = {"sources_sha256_16": "d0d74530d64fcf9a", "bytes": 130371589}
+# Valid only for the kernel code it was measured on: reported as null once that changes.
+GATE_UP_TRAFFIC = {"sources_sha256_16": "5127e244b5b7bc15", "bytes": 130371589}
 
 
 def gemv_sources_hash() -> str:
+    """Hash of the GEMV kernel sources with comments and whitespace removed, so that the guard
+    follows the code, not its commentary."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "nvfp4_weight_only_rtn_amd", "csrc")
-    data = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("gemv.hip", "attnq_device.h"))
-    return hashlib.sha256(data).hexdigest()[:16]
+    code = "".join(open(os.path.join(csrc, f)).read() for f in ("gemv.hip", "attnq_device.h"))
+    code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+    code = re.sub(r"//[^\n]*", " ", code)
+    code = re.sub(r"\s+", " ", code)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def nvfp4_bytes(N: int, K: int, n_seg: int) -> int:
