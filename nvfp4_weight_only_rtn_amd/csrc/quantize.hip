@@ -220,28 +220,52 @@ size_t lowrank_lds_bytes(int r) { return (size_t)min(r, kRankChunk) * (kVStride 
 // the next integer, far beyond its rounding error.
 __device__ __forceinline__ int div_small(int e, float inv_n) { return (int)(((float)e + 0.5f) * inv_n); }
 
-// Copy rows base .. base+nrow-1 (clamped to `limit`, zero past it) of a row-major [*, r] bf16 matrix,
-// columns k0 .. k0+kn-1, into LDS as fp32 dst[k * stride + row]. Consecutive threads read
-// consecutive elements; each thread issues its (up to) 8 loads before any LDS write.
-template <int NROW>
-__device__ __forceinline__ void stage_transposed(const uint16_t* __restrict__ src, int r, int base, int limit, int k0,
-                                                 int kn, float inv_kn, float* dst, int stride) {
-  const int total = NROW * kn;
-  for (int e0 = 0; e0 < total; e0 += 8 * 256) {
-    uint16_t v[8];
-    int at[8];
+// Stage columns k0 .. k0+kn-1 of the tile's V rows (col0 .. col0+255, zero past K) and U rows
+// (row0 .. row0+63, zero past N) into LDS as fp32 vt[k * kVStride + column] and
+// ut[k * kUStride + row]. The two are one flat element space (V first); consecutive threads read
+// consecutive elements, and each thread issues up to kStageBatch loads before any LDS write, so a
+// rank chunk of up to 16 is staged in one round trip. Only the loaded values stay live across
+// the batch; each element's place is worked out again when it is written.
+constexpr int kStageBatch = 20;
+
+struct StageElem {
+  const uint16_t* src;
+  int index;        // element of src, clamped into the matrix
+  int slot;         // LDS float index relative to vt
+  bool inside;      // false: the row is past the matrix, the slot takes 0
+};
+
+__device__ __forceinline__ StageElem stage_elem(const Theta& t, int row0, int col0, int k0, int kn, float inv_kn,
+                                                int nv, int e, int u_off) {
+  const bool is_v = e < nv;
+  const int f = is_v ? e : e - nv;
+  const int row = div_small(f, inv_kn), k = f - row * kn;
+  const int base = is_v ? col0 : row0, limit = is_v ? t.K : t.N;
+  StageElem s;
+  s.src = is_v ? t.V : t.U;
+  s.index = min(base + row, limit - 1) * t.r + k0 + k;
+  s.slot = is_v ? k * kVStride + row : u_off + k * kUStride + row;
+  s.inside = base + row < limit;
+  return s;
+}
+
+__device__ __forceinline__ void stage_uv(const Theta& t, int row0, int col0, int k0, int kn, float inv_kn, float* vt,
+                                         float* ut) {
+  const int nv = kTileCols * kn, total = (kTileCols + kTileRows) * kn;
+  const int u_off = (int)(ut - vt);
+  for (int e0 = 0; e0 < total; e0 += kStageBatch * 256) {
+    uint16_t v[kStageBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {                 // clamped, branch-free loads, all issued first
-      const int e = min(e0 + j * 256 + (int)threadIdx.x, total - 1);
-      const int row = div_small(e, inv_kn), k = e - row * kn;
-      v[j] = src[(size_t)min(base + row, limit - 1) * r + k0 + k];
-      at[j] = (base + row < limit) ? k * stride + row : ~(k * stride + row);
+    for (int j = 0; j < kStageBatch; ++j) {       // clamped, branch-free loads, all issued first
+      const StageElem s = stage_elem(t, row0, col0, k0, kn, inv_kn, nv, min(e0 + j * 256 + (int)threadIdx.x, total - 1), u_off);
+      v[j] = s.src[s.index];
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (e0 + j * 256 + (int)threadIdx.x < total) {
-        if (at[j] >= 0) dst[at[j]] = bf16_bits_to_f32(v[j]);
-        else dst[~at[j]] = 0.0f;
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int e = e0 + j * 256 + (int)threadIdx.x;
+      if (e < total) {
+        const StageElem s = stage_elem(t, row0, col0, k0, kn, inv_kn, nv, e, u_off);
+        vt[s.slot] = s.inside ? bf16_bits_to_f32(v[j]) : 0.0f;
       }
     }
   }
@@ -290,9 +314,7 @@ __global__ __launch_bounds__(256) void k_lowrank_tile(Theta t, uint32_t* slot, u
     if (k0 > 0) __syncthreads();                 // previous chunk fully consumed
     // stage V (tile columns) and U (tile rows) for k0 .. k0+kn-1, transposed to [k][.]; zero
     // outside the matrix
-    const float inv_kn = 1.0f / (float)kn;
-    stage_transposed<kTileCols>(t.V, r, col0, t.K, k0, kn, inv_kn, vt, kVStride);
-    stage_transposed<kTileRows>(t.U, r, row0, t.N, k0, kn, inv_kn, ut, kUStride);
+    stage_uv(t, row0, col0, k0, kn, 1.0f / (float)kn, vt, ut);
     __syncthreads();
     for (int k = 0; k < kn; ++k) {               // k ascending: one fp32 rounding per step
       const f32x4* vp = reinterpret_cast<const f32x4*>(vt + k * kVStride + cb * kBlock);
