@@ -553,6 +553,55 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
   }
 }
 
+// bf16 weights, one-shot (rows of at most S x 64 chunks of 8 elements): a wave owns R rows and
+// issues every weight and x load of them (S steps) before computing.
+template <int R, int S, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_bf16_oneshot(const uint16_t* __restrict__ W,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  float* __restrict__ y, int N, int K) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wave) * R;
+  const int cpr = K >> 3;
+  const u32x4* xg = reinterpret_cast<const u32x4*>(x);
+  u32x4 xv[S], wv[S][R];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = min(s * 64 + lane, cpr - 1);
+    xv[s] = xg[c];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(row0 + r, N - 1);
+      wv[s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)row * K) + c);
+    }
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (s * 64 + lane < cpr) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float a = acc[r];
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].x), as_bf16x2(xv[s].x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].y), as_bf16x2(xv[s].y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].z), as_bf16x2(xv[s].z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].w), as_bf16x2(xv[s].w), a, false);
+        acc[r] = a;
+      }
+    }
+  }
+  wave_sums<R>(acc);
+  if (lane < R) {
+    float v = acc[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
+    const int row = row0 + lane;
+    if (row < N) y[row] = v;
+  }
+}
+
 // part[g][p][k] = sum over the rows j of chunk p of x[j] V[g][j][k] (V [n_seg][K][r] bf16), one
 // workgroup per (chunk, segment); a chunk is floor(16384 / r) rows of V.
 //
@@ -853,6 +902,17 @@ bool launch_gemm_nvfp4_tokens(const attnq_nvfp4& W, const uint16_t* X, int M, in
 
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream) {
   if (N == 0) return hipSuccess;
+  // rows of up to 4096 / 5632 elements: one row per wave, every load issued at once (8 / 11 steps);
+  // longer rows walk K two rows per wave, four chunks in flight
+  const int cpr = K / 8;
+  if (cpr <= 512) {
+    k_gemv_bf16_oneshot<1, 8, 4><<<(N + 3) / 4, 256, 0, stream>>>(W, x, y, N, K);
+    return hipGetLastError();
+  }
+  if (cpr <= 704) {
+    k_gemv_bf16_oneshot<1, 11, 4><<<(N + 3) / 4, 256, 0, stream>>>(W, x, y, N, K);
+    return hipGetLastError();
+  }
   constexpr int R = 2;
   const unsigned grid = (unsigned)((N + 4 * R - 1) / (4 * R));
   k_gemv_bf16<R><<<grid, 256, 0, stream>>>(W, x, y, N, K);
