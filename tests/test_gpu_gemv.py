@@ -135,7 +135,10 @@ def test_gemv_empty_is_noop(A):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("N,K", [(1, 32), (7, 64), (1000, 1152), (4096, 5376), (333, 21504)])
+# launch classes of the bf16 GEMV: one-shot with 8 steps (K <= 4096), 11 steps (K <= 5632), the loop
+# kernel beyond; each boundary from both sides
+@pytest.mark.parametrize("N,K", [(1, 32), (7, 64), (1000, 1152), (4096, 5376), (333, 21504),
+                                 (301, 4096), (301, 4096 + 32), (301, 5632), (301, 5632 + 32)])
 def test_gemv_bf16(A, N, K):
     W = inputs.normal_bf16((N, K), 0.02, 9, 33, N, 0)
     x = inputs.activation_bf16(1, K, 9, 33, N)
@@ -172,9 +175,11 @@ def test_small_m(A, M):
 
 
 # ragged K (K % 128 in {32, 64, 96} exercises the 32-element tail), ragged 16-row tiles, both
-# launch configurations (N >= 16384 uses two row tiles per wave), and every token-row count class
+# launch configurations (N >= 16384 uses two row tiles per wave), every token-row count class, and
+# M <= 4 on either side of the batch-1 walk's row limit (6144 elements)
 @pytest.mark.parametrize("N,K,M", [(1, 32, 1), (17, 96, 3), (333, 1184, 16), (1000, 1248, 5), (4097, 2080, 8),
-                                   (16385, 224, 4), (16400, 1152 + 64, 13), (600, 21504 + 32, 2)])
+                                   (16385, 224, 4), (16400, 1152 + 64, 13), (600, 21504 + 32, 2),
+                                   (301, 6144, 3), (301, 6144 + 32, 4)])
 def test_small_m_ragged(A, N, K, M):
     b = inputs.theta_bundle(N, K, 0, cfg=9, layer=31, proj=N % 97, passthrough=True)
     say(f"small-M ragged {M}x{N}x{K}")
@@ -189,8 +194,11 @@ def test_small_m_ragged(A, N, K, M):
 
 
 # rows of at most 192 chunks: M <= 4 runs on the batch-1 walk, and each token's row is the batch-1
-# GEMV of that token bit for bit (same launch shape, same per-block arithmetic and wave sums)
-@pytest.mark.parametrize("N,K", [(4097, 2080), (5376, 4096), (6144, 5376), (16400, 5376), (300, 96)])
+# GEMV of that token bit for bit (same launch shape, same per-block arithmetic and wave sums); the
+# shapes straddle its class boundaries (two steps up to K = 4096, three up to 6144, one row per wave
+# below N = 16384 and two from there)
+@pytest.mark.parametrize("N,K", [(4097, 2080), (5376, 4096), (6144, 5376), (16400, 5376), (300, 96),
+                                 (301, 4096 + 32), (16383, 6144), (16384, 4096 + 32)])
 def test_small_m_tokens_equal_the_gemv_bitwise(A, N, K):
     say(f"small-M vs GEMV bitwise {N}x{K}")
     b = inputs.theta_bundle(N, K, 0, cfg=9, layer=37, proj=0, passthrough=True)
