@@ -1,4 +1,6 @@
-// Decode GEMVs y = x * W^T at batch 1: the NVFP4 weight-streaming kernel and the bf16 one.
+// Decode GEMVs y = x * W^T: the NVFP4 weight-streaming kernels at batch 1 (plain, with the gate|up
+// activation epilogue, with the runtime low-rank epilogue and its partial-sum kernels), the same
+// walk for 1 <= M <= 4 tokens (k_gemm_nvfp4_tokens), and the bf16 kernels.
 //
 // "GPU acceleration", "Where GPU time goes": batch-1 decode is dominated by GEMVs that read
 // every weight once, and the block-scaled kernel consumes fp4 directly (no dequant launch).
