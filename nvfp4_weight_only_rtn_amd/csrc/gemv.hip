@@ -904,15 +904,16 @@ bool launch_gemm_nvfp4_tokens(const attnq_nvfp4& W, const uint16_t* X, int M, in
 
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  // rows of up to 4096 / 5632 elements: one row per wave, every load issued at once (8 / 11 steps);
+  // rows of up to 4096 / 5632 elements: one row per wave, every load issued at once (8 / 11 steps),
+  // eight waves per workgroup (measured ahead of 2, 4 and 16 on the lm_head and q|k|v shapes);
   // longer rows walk K two rows per wave, four chunks in flight
   const int cpr = K / 8;
   if (cpr <= 512) {
-    k_gemv_bf16_oneshot<1, 8, 4><<<(N + 3) / 4, 256, 0, stream>>>(W, x, y, N, K);
+    k_gemv_bf16_oneshot<1, 8, 8><<<(N + 7) / 8, 512, 0, stream>>>(W, x, y, N, K);
     return hipGetLastError();
   }
   if (cpr <= 704) {
-    k_gemv_bf16_oneshot<1, 11, 4><<<(N + 3) / 4, 256, 0, stream>>>(W, x, y, N, K);
+    k_gemv_bf16_oneshot<1, 11, 8><<<(N + 7) / 8, 512, 0, stream>>>(W, x, y, N, K);
     return hipGetLastError();
   }
   constexpr int R = 2;
