@@ -126,7 +126,11 @@ ATTNQ_API attnq_status attnq_quantize_nvfp4(const attnq_theta* theta, const attn
 /* y[n] = sum_k x[k] * weight[n][k] for an NVFP4 weight: one kernel that reads codes and
  * scales once and decodes fp4 in registers ("Where GPU time goes": no dequant pass).
  * x [K] bf16 16-byte aligned; y [N] fp32 4-byte aligned, must not overlap x or the weight.
- * Accumulation is fp32. */
+ * Accumulation is fp32. Errors (checked on the host, nothing launched): ATTNQ_ERR_NULL for a NULL
+ * weight, tensor_scale or x, or NULL codes / scales / y with N > 0; ATTNQ_ERR_LAYOUT for an
+ * unknown layout; ATTNQ_ERR_SHAPE for N < 0, K not a positive multiple of 32 or N * K/2 > 2^32;
+ * ATTNQ_ERR_SEGMENT for a segment table that is not strictly increasing up to N;
+ * ATTNQ_ERR_ALIGN for a misaligned pointer; ATTNQ_ERR_HIP if the launch fails. */
 ATTNQ_API attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y,
                               attnq_stream stream);
 
@@ -181,16 +185,22 @@ ATTNQ_API attnq_status attnq_gemv_nvfp4_lowrank(const attnq_nvfp4* W0, const uin
  * only, no GPU call. */
 ATTNQ_API int64_t attnq_gemv_nvfp4_lowrank_workspace(int32_t K, int32_t n_seg, int32_t r);
 
-/* y[n] = sum_k x[k] * W[n][k] for a bf16 weight [N][K] (the tied lm_head, or projections
- * left in bf16). W and x 16-byte aligned, y 4-byte aligned. fp32 accumulation. */
+/* y[n] = sum_k x[k] * W[n][k] for a bf16 weight [N][K], row-major: the tied lm_head, which the
+ * pages keep in bf16, and projections left in bf16 ("Where GPU time goes": the bf16 GEMV
+ * families next to the NVFP4 ones). W and x 16-byte aligned, y 4-byte aligned and not
+ * overlapping W or x; fp32 accumulation. Errors: ATTNQ_ERR_SHAPE for N < 0 or K not a positive
+ * multiple of 32; ATTNQ_ERR_NULL for a NULL x, or a NULL W / y with N > 0; ATTNQ_ERR_ALIGN;
+ * ATTNQ_ERR_HIP if the launch fails. */
 ATTNQ_API attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, const uint16_t* x, float* y,
                              attnq_stream stream);
 
 /* Y[m][n] = sum_k X[m][k] * weight[n][k] for 0 <= M <= 16 token rows (speculative verify at
  * gamma + 1 = 4, batch 8). X row m at X + m*ldx (bf16, ldx >= K, ldx % 8 == 0, X 16-byte
  * aligned, (M - 1)*ldx + K < 2^30); Y row m at Y + m*ldy (fp32, ldy >= N, Y 4-byte aligned).
- * Uses MFMA matrix cores; fp32 accumulation. Errors: as attnq_gemv_nvfp4; M outside [0, 16] or
- * a stride or extent out of range is ATTNQ_ERR_SHAPE. */
+ * M <= 4 with rows of at most 6144 elements runs the batch-1 GEMV walk (each row of Y then equals
+ * attnq_gemv_nvfp4 of that token bit for bit); other shapes use the MFMA matrix cores. fp32
+ * accumulation. Errors: as attnq_gemv_nvfp4; M outside [0, 16] or a stride or extent out of
+ * range is ATTNQ_ERR_SHAPE. */
 ATTNQ_API attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, int32_t M,
                                       int32_t ldx, float* Y, int32_t ldy, attnq_stream stream);
 
