@@ -265,9 +265,9 @@ __global__ __launch_bounds__(256) void k_gemv_nvfp4(const uint8_t* __restrict__ 
 // One-shot variant for rows of at most S*64 chunks per wave slice: every wave issues the code
 // and scale loads of its whole slice (S steps x R rows) before computing, which keeps the most
 // bytes in flight per wave. With XL the workgroup stages x in LDS once, transposed so that the
-// four 16-byte quarter reads of a chunk ([q][chunk]) are each bank-conflict free. XFIRST loads x
-// (at most XI 16-byte pieces per thread) into registers ahead of the weight loads; without it, x
-// is loaded after them in a plain loop. The LDS store of a piece is guarded (pieces past x are
+// four 16-byte quarter reads of a chunk ([q][chunk]) and the staging stores are bank-conflict
+// free. XFIRST loads x (at most XI 16-byte pieces per thread) into registers ahead of the weight
+// loads; without it, x is loaded after them in a plain loop. The LDS store of a piece is guarded (pieces past x are
 // skipped), and the compiler moves the load of a thread's first piece into that guarded store,
 // behind the weight loads, so the staging waits for all of the wave's loads. A branch-free store
 // that keeps every x load first, so that the staging waits for x alone, measured slower inside
@@ -282,9 +282,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   static_assert(WAVES % KSPLIT == 0, "K split must divide the waves of a workgroup");
   static_assert(!XFIRST || XL, "x-first staging is an LDS staging");
   static_assert(EPI != 1 || (R == 2 && KSPLIT == 1), "the gate|up epilogue takes one row pair per wave");
-  // x in LDS as [quarter][chunk] with a compile-time pitch (the longest row the kernel takes,
-  // KSPLIT x S x 64 chunks), so the four quarter reads of a chunk use immediate offsets
-  constexpr int kPitch = KSPLIT * S * 64;
+  // x in LDS as [quarter][chunk] with a compile-time pitch, so the four quarter reads of a chunk
+  // use immediate offsets: the longest row the kernel takes (KSPLIT x S x 64 chunks) plus 4
+  // entries, which moves each quarter by 64 bytes across the banks. Without the pad the quarters
+  // start a multiple of 256 bytes apart, and the staging store, whose four lanes per chunk write
+  // the four quarters, is a 4-way bank conflict (SQ_LDS_BANK_CONFLICT); the quarter reads are
+  // 1 KiB contiguous per wave either way.
+  constexpr int kPitch = KSPLIT * S * 64 + 4;
   __shared__ u32x4 xs[XL ? 4 * kPitch : 1];
   constexpr int kRowGroups = WAVES / KSPLIT;
   const int lane = threadIdx.x & 63;
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_nvfp4_tokens(const uint8_t*
                                                                   SegTable segs, const uint16_t* __restrict__ X,
                                                                   int ldx, float* __restrict__ Y, int ldy, int N,
                                                                   int K) {
-  constexpr int kPitch = S * 64;
+  constexpr int kPitch = S * 64 + 4;        // padded as in the batch-1 kernel (conflict-free staging)
   __shared__ u32x4 xs[MT][4 * kPitch];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
