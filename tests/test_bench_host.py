@@ -67,7 +67,8 @@ def test_traffic_figure_matches_the_committed_counter_summary():
     assert abs(scaled / algorithmic - 1.0) < 0.01
 
 
-@pytest.mark.parametrize("name", ["gemv_nvfp4_31b_token_kernel_stats.md", "gemv_nvfp4_31b_token_traffic.md"])
+@pytest.mark.parametrize("name", ["gemv_nvfp4_31b_token_kernel_stats.md", "gemv_nvfp4_31b_token_traffic.md",
+                                  "gemv_nvfp4_31b_token_sq_counters.md"])
 def test_profile_summaries_name_their_commands(name):
     text = open(os.path.join(ROOT, "profiles", name)).read()
     assert "rocprofv3" in text and "bench.py" in text
