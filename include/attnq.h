@@ -8,8 +8,8 @@
  *     Precompute-outside (the fast path)".
  *   - NVFP4 round-to-nearest quantization at load, packed uint8 codes plus float8 block
  *     scales: "GPU acceleration", "NVFP4 quantization"; landing page, "Results";
- *     "Throughput", "What quantization actually saves" (one float8_e4m3fn scale per 16
- *     elements, 0.5625 B per element).
+ *     "Throughput", "What quantization actually saves" (an E4M3 scale byte for each block
+ *     of 16 elements, 0.5625 B per element).
  *   - the decode GEMVs that consume fp4 directly with no dequant pass, fused Q/K/V, the bf16
  *     tied lm_head: "GPU acceleration", "Where GPU time goes" and "Q/K/V fusion";
  *     "Throughput", "The NVFP4 MLP kernels are the least bandwidth-efficient on the step".
@@ -148,7 +148,8 @@ ATTNQ_API attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x,
  * Q/K/V fusion). W holds two segments of F = N/2 rows each, gate rows then up rows
  * (seg_end = {F, N}). For j < F:
  *   g_j = sum_k x[k] * weight[j][k],  u_j = sum_k x[k] * weight[F + j][k]   (fp32, as in
- *         attnq_gemv_nvfp4, whose y[j] and y[F + j] they equal bit for bit),
+ *         attnq_gemv_nvfp4; for rows of up to 6144 elements they equal its y[j] and y[F + j]
+ *         bit for bit, longer rows add their partial sums in another order),
  *   h[j] = bf16_rne(fl32(act(g_j) * u_j)), the activation evaluated in fp32.
  * One kernel, no fp32 y round trip. x [K] bf16 16-byte aligned; h [F] bf16 2-byte aligned, must
  * not overlap x or the weight.

@@ -4,7 +4,7 @@
 // weightless "GPU and cache acceleration", "Precompute-outside". Quantization: "GPU
 // acceleration", "NVFP4 quantization" (packed uint8 plus float8 block scales, at load);
 // landing page "Results" (round-to-nearest, no calibration); "Throughput", "What quantization
-// actually saves" (one float8_e4m3fn scale per 16 elements).
+// actually saves" (an E4M3 scale byte for each block of 16 elements).
 //
 // Rank 0 (passthrough or row scale only): one thread owns one 16-element block of a row, rebuilds
 // it in registers, rounds it to bf16 and then either folds |w| into the segment amax or emits 8

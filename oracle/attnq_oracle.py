@@ -15,10 +15,11 @@ What it computes, and where each step is defined:
 * NVFP4 round-to-nearest quantization -- "GPU acceleration", "NVFP4
   quantization" (packed uint8 weights plus float8 block scales, quantized once
   at load); landing page, "Results" (round-to-nearest, no calibration);
-  "Throughput", "What quantization actually saves" (0.5 B of packed weight plus
-  one float8_e4m3fn scale per 16 elements = 0.5625 B/element). The E2M1 value
-  grid and the FP32 per-tensor scale are not printed on the pages; they are
-  the NVFP4 format itself (E2M1 = 1 sign, 2 exponent, 1 mantissa bit).
+  "Throughput", "What quantization actually saves" (storage cost: four bits
+  per element plus an E4M3 scale byte for every 16-element block, 0.5625
+  B/element). The E2M1 value grid and the FP32 per-tensor scale are not
+  printed on the pages; they are the NVFP4 format itself (E2M1 = 1 sign,
+  2 exponent, 1 mantissa bit).
 * The decode GEMV ``y = x * W_eff^T`` consuming fp4 directly -- "GPU
   acceleration", "Where GPU time goes" (weight-reading GEMVs, no dequant
   kernel) and "Throughput", "The NVFP4 MLP kernels are the least
@@ -29,8 +30,9 @@ What it computes, and where each step is defined:
   The pages do not name the activation; GELU with the tanh approximation,
   SiLU and the identity are offered. Reading: the activation and product are
   evaluated in float64 on the float64 GEMV outputs and rounded once to bf16
-  (PARITY PINNED by closed forms, odd-part identities and a library
-  cross-check in tests/test_oracle_glu.py).
+  (PARITY PINNED by closed forms, odd-part identities, a library cross-check
+  and a hand-built two-segment weight whose gate/up pairing is checked, in
+  tests/test_oracle_glu.py).
 * The runtime low-rank product over a shared NVFP4 block, ``y = s * (x .
   deq(W0)^T) + U (V_g^T x)`` with the weight never rebuilt -- "Throughput",
   "The runtime reconstruction path does not reach dense parity" (W0 and the
@@ -48,7 +50,10 @@ design notes of the repository):
   ``acc = 0; acc += U[i,k]*V[j,k]`` for k ascending, then ``s_i*W0[i,j] + acc``
   rounded once to fp32 and once to bf16; with r == 0 the add is skipped.
   bf16 x bf16 products are exact in fp32, so a fused multiply-add gives the
-  same bits.
+  same bits. (PARITY PINNED: this sequence is checked element by element
+  against exact rational arithmetic with explicit IEEE rounding steps on
+  bundles where the order decides the result, and by a hand-derived example,
+  in tests/test_oracle_reconstruct_order.py.)
 * quantization starts from the bf16 W_eff (also when reconstruction is fused).
 * tensor scale ``ts = fl32(amax / 2688)`` (2688 = 6 * 448, the E2M1 maximum
   times the E4M3 maximum), one per projection ("segment"), stored as the

@@ -75,3 +75,37 @@ def test_f64_to_bf16_matches_exact_rounding_on_random_values():
     pick = np.where((is_min & (cand % 2 == 0)).any(axis=0), np.argmax(is_min & (cand % 2 == 0), axis=0),
                     np.argmax(is_min, axis=0))
     assert np.array_equal(got.astype(np.int64), cand[pick, np.arange(a.size)])
+
+
+def test_hand_built_gate_up_pairs():
+    """A two-segment [gate; up] weight built by hand (K = 32, F = 2 pairs), through the oracle's
+    fused GEMV and its SiLU epilogue. Tensor scales: gate 0.5, up 2.0; E4M3 block scale 0x38 = 1.0,
+    except block 0 of up row 1, 0x30 = 0.5. Codes (sign<<3 | index into 0 .5 1 1.5 2 3 4 6, the
+    even element in the low nibble of a byte):
+      gate row 0: element 0 = 4   (code 0x6, byte 0 = 0x06) -> g0 = 4 * 1 * 0.5 = 2
+      gate row 1: element 1 = -2  (code 0xC, byte 0 = 0xC0) -> g1 = -2 * 1 * 0.5 = -1
+      up row 0:   element 0 = 1.5 (code 0x3, byte 0 = 0x03) -> u0 = 1.5 * 1 * 2 = 3
+      up row 1:   element 1 = 0.5 (code 0x1, byte 0 = 0x10) -> u1 = 0.5 * 0.5 * 2 = 0.5
+    with x = e0 + e1. SiLU(g) = g / (1 + e^-g):
+      h0 = SiLU(2) * 3 = 5.2847824...; bf16 step in [4, 8) is 2^-5: 169.11 steps -> 169 * 2^-5 =
+           5.28125 = 0x40A9 (swapping gate and up gives SiLU(3) * 2 = 5.7154 -> 0x40B7);
+      h1 = SiLU(-1) * 0.5 = -0.1344707...; step in [1/8, 1/4) is 2^-10: 137.70 steps -> 138 * 2^-10
+           = 0.134765625, negative: 0xBE0A (swapped: SiLU(0.5) * -1 = -0.3112 -> 0xBE9F).
+    The identity epilogue gives the exact products 6 = 0x40C0 and -0.5 = 0xBF00."""
+    codes = np.zeros((4, 16), np.uint8)
+    codes[0, 0], codes[1, 0], codes[2, 0], codes[3, 0] = 0x06, 0xC0, 0x03, 0x10
+    scales = np.full((4, 2), 0x38, np.uint8)
+    scales[3, 0] = 0x30
+    ts = np.array([0.5, 2.0], np.float32)
+    x = np.zeros(32, np.uint16)
+    x[0] = x[1] = 0x3F80
+    g, u = O.gemv_nvfp4_glu(codes, scales, ts, x)
+    assert list(g) == [2.0, -1.0] and list(u) == [3.0, 0.5]
+    assert list(O.glu(g, u, O.ACT_SILU)) == [0x40A9, 0xBE0A]
+    assert list(O.glu(g, u, O.ACT_IDENTITY)) == [0x40C0, 0xBF00]
+    # the hand values against the rounding of a float64 evaluation (math.exp, a library routine)
+    import math
+    for gv, uv, want in ((2.0, 3.0, 0x40A9), (-1.0, 0.5, 0xBE0A), (3.0, 2.0, 0x40B7), (0.5, -1.0, 0xBE9F)):
+        h = gv / (1.0 + math.exp(-gv)) * uv
+        step = 2.0 ** (math.floor(math.log2(abs(h))) - 7)
+        assert O.bf16_to_f32(np.array([want], np.uint16))[0] == np.float32(round(h / step) * step)

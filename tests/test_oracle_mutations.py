@@ -151,3 +151,81 @@ def test_lowrank_first_segment_factors_everywhere_are_caught(monkeypatch):
     import test_oracle_lowrank as PL
     _lowrank_mutant(monkeypatch, lambda y, s, x, U, V, seg: s * y + _delta(U, V, x, np.zeros_like(seg)))
     assert _fails(PL.test_lowrank_equals_exact_rational_sum)
+
+
+# ---------------------------------------------------------------------------------------------
+# the rebuild's rounding sequence (s*W0 + U V^T at rank r > 0)
+# ---------------------------------------------------------------------------------------------
+def _rebuild_mutant(monkeypatch, combine):
+    """Replace the oracle's rebuild at r > 0 by one whose fp32 sequence is `combine(base, u, v)`."""
+    orig = OM.reconstruct
+
+    def mutated(W0, s=None, U=None, V=None):
+        if U is None or U.shape[1] == 0:
+            return orig(W0, s)
+        w0 = OM.bf16_to_f32(W0)
+        sv = np.ones(w0.shape[0], np.float32) if s is None else OM.bf16_to_f32(s)
+        base = (sv[:, None] * w0).astype(np.float32)
+        return OM.f32_to_bf16_rne(combine(base, OM.bf16_to_f32(U), OM.bf16_to_f32(V)))
+    monkeypatch.setattr(OM, "reconstruct", mutated)
+    monkeypatch.setattr(O, "reconstruct", mutated)
+
+
+def _order_pins_fail():
+    import test_oracle_reconstruct_order as PO
+    return (_fails(PO.test_worked_example_where_the_order_decides) or
+            _fails(PO.test_exact_rounding_sequence_on_cancellation_bundles, 16))
+
+
+def test_rebuild_with_base_added_first_is_caught(monkeypatch):
+    def base_first(base, u, v):
+        w = base.copy()
+        for k in range(u.shape[1]):
+            w = (w + u[:, k][:, None] * v[:, k][None, :]).astype(np.float32)
+        return w
+    _rebuild_mutant(monkeypatch, base_first)
+    assert _order_pins_fail()
+
+
+def test_rebuild_summed_in_float64_and_rounded_once_is_caught(monkeypatch):
+    def once(base, u, v):
+        return (base.astype(np.float64) + u.astype(np.float64) @ v.astype(np.float64).T).astype(np.float32)
+    _rebuild_mutant(monkeypatch, once)
+    assert _order_pins_fail()
+
+
+def test_rebuild_with_rank_terms_descending_is_caught(monkeypatch):
+    def descending(base, u, v):
+        acc = np.zeros(base.shape, np.float32)
+        for k in reversed(range(u.shape[1])):
+            acc = (acc + u[:, k][:, None] * v[:, k][None, :]).astype(np.float32)
+        return (base + acc).astype(np.float32)
+    _rebuild_mutant(monkeypatch, descending)
+    assert _fails(__import__("test_oracle_reconstruct_order").test_exact_rounding_sequence_on_cancellation_bundles, 16)
+
+
+# ---------------------------------------------------------------------------------------------
+# the gate|up pairing of the fused epilogue
+# ---------------------------------------------------------------------------------------------
+def test_gate_and_up_swapped_is_caught(monkeypatch):
+    import test_oracle_glu as PGL
+    orig = OM.gemv_nvfp4_glu
+
+    def swapped(codes, scales, ts, x_bf16, rows=None):
+        g, u = orig(codes, scales, ts, x_bf16, rows)
+        return u, g
+    monkeypatch.setattr(OM, "gemv_nvfp4_glu", swapped)
+    monkeypatch.setattr(O, "gemv_nvfp4_glu", swapped)
+    assert _fails(PGL.test_hand_built_gate_up_pairs)
+
+
+def test_gate_up_pairs_shifted_is_caught(monkeypatch):
+    import test_oracle_glu as PGL
+    orig = OM.gemv_nvfp4_glu
+
+    def shifted(codes, scales, ts, x_bf16, rows=None):
+        g, u = orig(codes, scales, ts, x_bf16, rows)
+        return g, np.roll(u, 1)
+    monkeypatch.setattr(OM, "gemv_nvfp4_glu", shifted)
+    monkeypatch.setattr(O, "gemv_nvfp4_glu", shifted)
+    assert _fails(PGL.test_hand_built_gate_up_pairs)
