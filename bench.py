@@ -114,6 +114,12 @@ class Model:
         self.h = [torch.empty(GU_SEGS[0], dtype=torch.bfloat16, device=dev) for _ in range(N_LAYERS)]
         self.attn_bf16 = None
         self.lowrank = None
+        # one zeroed workspace serves every down projection (attnq_gemv_nvfp4_splitk), in stream order
+        self.ws = A.splitk_workspace(DOWN_SHAPE[0], DOWN_SHAPE[1], device=dev)
+
+    def down(self, W, x, y):
+        """The down projection (rows of 21504 elements): K split across workgroups."""
+        self.A.attnq_gemv_nvfp4_splitk(W, x, y, self.ws)
 
     def quantize_passthrough(self, dev):
         """Fill every NVFP4 weight from a seeded device bf16 W0 (passthrough reconstruction)."""
@@ -131,9 +137,10 @@ class Model:
     def step(self):
         A = self.A
         for lay in self.layers:
-            for name in PROJ_NAMES:
+            for name in PROJ_NAMES[:3]:
                 W, x, y, _, _ = lay[name]
                 A.attnq_gemv_nvfp4(W, x, y)
+            self.down(*lay["down"][:3])
         A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
 
     def glu_step(self):
@@ -147,7 +154,7 @@ class Model:
             W, x, _, _, _ = lay["gate_up"]
             A.attnq_gemv_nvfp4_glu(W, x, A.ACT_GELU_TANH, self.h[L])
             W, _, y, _, _ = lay["down"]
-            A.attnq_gemv_nvfp4(W, self.h[L], y)
+            self.down(W, self.h[L], y)
         A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
 
     def build_bf16_attention(self, dev):
@@ -166,9 +173,9 @@ class Model:
             qkv, o = self.attn_bf16[L]
             A.attnq_gemv_bf16(qkv, lay["qkv"][1], lay["qkv"][2])
             A.attnq_gemv_bf16(o, lay["o"][1], lay["o"][2])
-            for name in ("gate_up", "down"):
-                W, x, y, _, _ = lay[name]
-                A.attnq_gemv_nvfp4(W, x, y)
+            W, x, y, _, _ = lay["gate_up"]
+            A.attnq_gemv_nvfp4(W, x, y)
+            self.down(*lay["down"][:3])
         A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
 
     def build_lowrank(self, dev):
@@ -267,14 +274,7 @@ def time_steps(fn, steps: int) -> float:
 
 def graph_timing(fn, warmup: int, steps: int) -> float:
     """ms per step of `fn` captured once as a hipGraph and replayed."""
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn()
-    torch.cuda.current_stream().wait_stream(s)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        fn()
+    graph = graph_of(fn)
     for _ in range(max(1, warmup)):
         graph.replay()
     torch.cuda.synchronize()
@@ -284,23 +284,13 @@ def graph_timing(fn, warmup: int, steps: int) -> float:
 
 
 def dominant_kernel_timing(model: Model, reps: int):
-    """Average duration of the fused gate|up NVFP4 GEMV (the largest byte share of a token):
-    HIP events on the launch stream bracket `reps` back-to-back passes over the 60 layers'
-    distinct gate|up weights (7.8 GB per pass, so every launch streams from HBM)."""
+    """Average duration of the fused gate|up NVFP4 GEMV (the largest byte share of a token): the 60
+    layers' distinct gate|up launches (7.8 GB per pass, so every launch streams from HBM) captured
+    as a hipGraph and replayed `reps` times between HIP events on the replay stream. Returns ms."""
     A = model.A
-    launches = [lay["gate_up"] for lay in model.layers]
-    for (W, x, y, _, _) in launches:                      # warm-up pass
-        A.attnq_gemv_nvfp4(W, x, y)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        for (W, x, y, _, _) in launches:
-            A.attnq_gemv_nvfp4(W, x, y)
-    e1.record()
-    torch.cuda.synchronize()
-    n = reps * len(launches)
-    return e0.elapsed_time(e1) / n, n
+    launches = [lambda W=W, x=x, y=y: A.attnq_gemv_nvfp4(W, x, y) for (W, x, y, _, _) in
+                (lay["gate_up"] for lay in model.layers)]
+    return per_launch_us(launches, reps) * 1e-3, reps * len(launches)
 
 
 def load_path_timing(A, dev, model: Model, reps: int = 1):
@@ -378,27 +368,211 @@ def small_m_timing(A, model: Model, steps: int):
     return out
 
 
+def machine_state():
+    """Other GPU processes (rocm-smi --showpids) and the clock levels (rocm-smi --showclocks), read
+    before this process touches the GPU: a busy box reads low, so the run records whether it was idle."""
+    import subprocess
+    out = {}
+    try:
+        r = subprocess.run(["rocm-smi", "--showpids"], capture_output=True, text=True, timeout=60)
+        txt = r.stdout + r.stderr
+        out["idle"] = "No KFD PIDs currently running" in txt
+        if not out["idle"]:
+            out["gpu_processes"] = [l.strip() for l in txt.splitlines() if l.strip() and l.strip()[0].isdigit()][:8]
+    except Exception as e:                      # rocm-smi missing or failing: say so, do not stop
+        out["idle"] = None
+        out["idle_check_error"] = str(e)[:200]
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=60)
+        out["clocks"] = [" ".join(l.split()) for l in r.stdout.splitlines() if "clock level" in l][:8]
+    except Exception as e:
+        out["clocks"] = f"unavailable: {str(e)[:200]}"
+    return out
+
+
+def summarize_trials(ms: list) -> dict:
+    v = sorted(ms)
+    return {"n": len(v), "median_ms": round(float(np.median(v)), 5), "min_ms": round(v[0], 5),
+            "max_ms": round(v[-1], 5), "all_ms": [round(t, 5) for t in ms]}
+
+
+def per_launch_us(fn_list, reps: int) -> float:
+    """Average duration of back-to-back launches: the launches of `fn_list` (each item one launch on
+    distinct buffers) captured once as a hipGraph, replayed `reps` times between two HIP events on
+    the stream the graph runs on -- the conditions of the token stream."""
+    def run():
+        for f in fn_list:
+            f()
+    g = graph_of(run)
+    ms = time_steps(g.replay, reps)
+    del g
+    return ms * 1e3 / len(fn_list)
+
+
+def per_projection_timing(model: Model, reps: int):
+    """Each projection class launched back to back over the 60 layers' distinct weights (cold), next to
+    the read ceiling of the same bytes: attnq_read_ceiling over each weight's codes and scales. The
+    token's ceiling is 60 x the per-layer ceilings + the lm_head's."""
+    A = model.A
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    ceil_layer_us = 0.0
+    for name in PROJ_NAMES:
+        lays = [lay[name] for lay in model.layers]
+        if name == "down":
+            gemv = [lambda W=W, x=x, y=y: model.down(W, x, y) for (W, x, y, _, _) in lays]
+            plain = [lambda W=W, x=x, y=y: A.attnq_gemv_nvfp4(W, x, y) for (W, x, y, _, _) in lays]
+        else:
+            gemv = [lambda W=W, x=x, y=y: A.attnq_gemv_nvfp4(W, x, y) for (W, x, y, _, _) in lays]
+            plain = None
+        reads = [lambda W=W: A.attnq_read_ceiling(W.codes, W.scales, sink) for (W, _, _, _, _) in lays]
+        W0 = lays[0][0]
+        nbytes = nvfp4_bytes(W0.N, W0.K, len(W0.seg_end))
+        us = per_launch_us(gemv, reps)
+        ceil = per_launch_us(reads, reps)
+        ceil_layer_us += ceil
+        out[name] = {"us": round(us, 3), "TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
+                     "read_ceiling_us": round(ceil, 3),
+                     "ceiling_TBps": round((W0.codes.numel() + W0.scales.numel()) / (ceil * 1e-6) / 1e12, 3)}
+        if plain is not None:
+            out[name]["single_workgroup_k_us"] = round(per_launch_us(plain, reps), 3)
+    head = [lambda: A.attnq_gemv_bf16(model.lm_head, model.x_head, model.y_head)]
+    head_us = per_launch_us(head, reps)
+    head_ceil = per_launch_us([lambda: A.attnq_read_ceiling(model.lm_head, None, sink)], reps)
+    out["lm_head"] = {"us": round(head_us, 3), "TBps": round(bf16_bytes(VOCAB, HIDDEN) / (head_us * 1e-6) / 1e12, 3),
+                      "read_ceiling_us": round(head_ceil, 3),
+                      "ceiling_TBps": round(2 * VOCAB * HIDDEN / (head_ceil * 1e-6) / 1e12, 3)}
+    token_ceiling_ms = (N_LAYERS * ceil_layer_us + head_ceil) * 1e-3
+    return out, token_ceiling_ms
+
+
+def single_projection_c0(A, dev, trials: int, steps: int):
+    """One 1024 x 1152 projection (W0 ~ N(0, 0.02^2), s = 1, U = V = 0 at rank 4: passthrough), quantized
+    by the library, then copied to 1600 distinct places (1.06 GB, beyond the 256 MB last-level
+    cache); one step is one GEMV on each copy in turn, replayed as a hipGraph. Latency-bound: the
+    headline is microseconds per GEMV."""
+    from nvfp4_weight_only_rtn_amd import inputs
+    N, K, copies = 1024, 1152, 1600
+    W0 = inputs.device_normal_bf16((N, K), 0.02, seed=11, device=dev)
+    zU = torch.zeros((N, 4), dtype=torch.bfloat16, device=dev)
+    zV = torch.zeros((K, 4), dtype=torch.bfloat16, device=dev)
+    ones = torch.ones(N, dtype=torch.bfloat16, device=dev)
+    src = A.NVFP4Weight.empty(N, K, [N], device=dev)
+    A.attnq_quantize_nvfp4(W0, ones, zU, zV, src, seg=0)
+    Ws = []
+    for _ in range(copies):
+        W = A.NVFP4Weight.empty(N, K, [N], device=dev)
+        W.codes.copy_(src.codes)
+        W.scales.copy_(src.scales)
+        W.tensor_scale.copy_(src.tensor_scale)
+        Ws.append(W)
+    x = torch.randn(K, device=dev, generator=torch.Generator(device=dev).manual_seed(12)).to(torch.bfloat16)
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+
+    def run():
+        for W in Ws:
+            A.attnq_gemv_nvfp4(W, x, y)
+    g = graph_of(run)
+    ms = [time_steps(g.replay, steps) for _ in range(trials)]
+    del g
+    nbytes = nvfp4_bytes(N, K, 1)
+    med = float(np.median(ms))
+    return {"what": "1024x1152 NVFP4 GEMV, passthrough weight, 1600 rotated copies (1.06 GB) in one hipGraph",
+            "us_per_gemv": round(med * 1e3 / copies, 4), "bytes_per_gemv": nbytes,
+            "TBps": round(nbytes * copies / (med * 1e-3) / 1e12, 4),
+            "trials_us_per_gemv": [round(t * 1e3 / copies, 4) for t in ms]}
+
+
+def small_stack_c1(A, dev, trials: int, steps: int):
+    """The 1B-like decoder stack: 26 layers of fused q|k|v 1536x1152 (1024 + 256 + 256), o 1152x1024,
+    gate|up 2 x 6912 x 1152 and down 1152x6912, each rebuilt as s * W0 + U V^T (s ~ U(0.9, 1.1), rank-4
+    U, V ~ N(0, 1e-3^2), W0 ~ N(0, 0.02^2)) and quantized by the library. Three distinct copies of
+    the stack (1.18 GB) are streamed in turn so that the 392 MB of one token do not sit in the
+    last-level cache; one step = one token through 26 layers (104 GEMVs)."""
+    from nvfp4_weight_only_rtn_amd import inputs
+    H, r = 1152, 4
+    specs = (("qkv", (1024, 256, 256), H), ("o", (H,), 1024), ("gate_up", (6912, 6912), H), ("down", (H,), 6912))
+    stacks = []
+    seed = 300_000
+    total = 0
+    for c in range(3):
+        layers = []
+        for L in range(26):
+            lay = []
+            for name, segs, K in specs:
+                W = A.NVFP4Weight.empty(sum(segs), K, list(np.cumsum(segs)), device=dev)
+                for i, n in enumerate(segs):
+                    W0 = inputs.device_normal_bf16((n, K), 0.02, seed=seed, device=dev)
+                    sv = inputs.device_uniform_bf16((n,), 0.9, 1.1, seed=seed + 1, device=dev)
+                    U = inputs.device_normal_bf16((n, r), 1e-3, seed=seed + 2, device=dev)
+                    V = inputs.device_normal_bf16((K, r), 1e-3, seed=seed + 3, device=dev)
+                    seed += 4
+                    A.attnq_quantize_nvfp4(W0, sv, U, V, W, seg=i)
+                x = torch.randn(K, device=dev, generator=torch.Generator(device=dev).manual_seed(seed)).to(torch.bfloat16)
+                y = torch.empty(W.N, dtype=torch.float32, device=dev)
+                lay.append((W, x, y))
+                if c == 0:
+                    total += nvfp4_bytes(W.N, K, len(segs))
+            layers.append(lay)
+        stacks.append(layers)
+    torch.cuda.synchronize()
+
+    def run():
+        for layers in stacks:
+            for lay in layers:
+                for (W, x, y) in lay:
+                    A.attnq_gemv_nvfp4(W, x, y)
+    g = graph_of(run)
+    ms = [time_steps(g.replay, steps) / 3 for _ in range(trials)]
+    del g
+    med = float(np.median(ms))
+    return {"what": "1B-like stack, 26 layers x (q|k|v 1536x1152, o 1152x1024, gate|up 13824x1152, down 1152x6912), "
+                    "rank-4 rebuild + RTN at load, 3 rotated copies",
+            "ms_per_token": round(med, 5), "bytes_per_token": total,
+            "TBps": round(total / (med * 1e-3) / 1e12, 4), "launches_per_token": 104,
+            "trials_ms": [round(t, 5) for t in ms]}
+
+
+def graph_of(fn):
+    """`fn`'s launches captured once as a hipGraph (after one eager warm-up on a side stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
 def cpu_baseline():
-    """The oracle's dequantize + float64 GEMV on a bounded sample of the same workload: the four
-    projections of one 31B-like layer (q|k|v, o, gate|up, down: 401.8 M weights, 226 MB NVFP4),
-    repeated until about 10 s have passed (at most 8 passes). The oracle's own quantization of
-    the sample is setup (threads over segments), not timed."""
+    """The oracle as it stands, on one host thread (BLAS limited to one thread; numpy's elementwise work
+    is single-threaded anyway), over a bounded sample of the same workload:
+      * dequantize + float64 GEMV over the four projections of one 31B-like layer (q|k|v 6144x5376,
+        o 5376x4096, gate|up 43008x5376, down 5376x21504: 226 MB NVFP4) -- the reported value;
+      * the oracle's RTN quantization of the fused q|k|v (33.0 M elements), as elements per second;
+      * the whole-token figure, SCALED: 60 x the layer's GEMV time + the bf16 lm_head GEMV over 16384
+        of its 262144 rows x 16;
+      * the load path, SCALED: the 410 bundles' 24.06 G elements at the measured quantization rate
+        (rank 0 rebuild; the rank-16 rebuild adds its U V^T on top).
+    The oracle's quantization of the layer sample is setup, run on threads and not timed."""
     import concurrent.futures as cf
 
     import oracle as O
     from nvfp4_weight_only_rtn_amd import inputs
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        blas = 1
+    from threadpoolctl import threadpool_limits
     specs = (("qkv", QKV_SEGS, HIDDEN), ("o", (O_SHAPE[0],), O_SHAPE[1]),
              ("gate_up", GU_SEGS, HIDDEN), ("down", (DOWN_SHAPE[0],), DOWN_SHAPE[1]))
     jobs = [(p, i, n, K) for p, (_, segs, K) in enumerate(specs) for i, n in enumerate(segs)]
+    W0s = {}
 
     def quantize(job):
         p, i, n, K = job
         W0 = inputs.theta_bundle(n, K, 0, cfg=2, layer=0, proj=10 * p + i, passthrough=True)[0]
+        W0s[job] = W0
         return job, O.quantize_segment(W0)
     with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         done = dict(ex.map(quantize, jobs))
@@ -411,18 +585,36 @@ def cpu_baseline():
         x = inputs.activation_bf16(1, K, 2, 0, p)
         work.append((codes, scales, ts, list(np.cumsum(segs)), x))
     nbytes = sum(c.nbytes + sc.nbytes + t.nbytes for c, sc, t, _, _ in work)
-    reps = 0
-    t0 = time.perf_counter()
-    while reps < 8 and (reps == 0 or time.perf_counter() - t0 < 10.0):   # about 10 s of CPU work
+    head_rows = 16384
+    head = inputs.normal_bf16((head_rows, HIDDEN), 0.02, 3, 60, 0, 0)
+    x_head = inputs.activation_bf16(1, HIDDEN, 3, 60, 0)
+    qkv_jobs = [(0, i, n, HIDDEN) for i, n in enumerate(QKV_SEGS)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
         for codes, scales, ts, ends, x in work:
             O.gemv_nvfp4(codes, scales, ts, x, ends)
-        reps += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes * reps / dt / 1e12, 9), "unit": "TB/s", "cores": int(blas), "kind": "oracle",
+        t_layer = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.gemv_bf16(head, x_head)
+        t_head = (time.perf_counter() - t0) * (VOCAB // head_rows)
+        t0 = time.perf_counter()
+        for job in qkv_jobs:
+            O.quantize_segment(W0s[job])
+        t_quant = time.perf_counter() - t0
+    q_elems = sum(n * HIDDEN for n in QKV_SEGS)
+    q_rate = q_elems / t_quant
+    return {"value": round(nbytes / t_layer / 1e12, 9), "unit": "TB/s", "cores": 1, "kind": "oracle",
             "sample": f"oracle dequantize + float64 GEMV over one 31B-like layer (q|k|v 6144x5376, o 5376x4096, "
-                      f"gate|up 43008x5376, down 5376x21504), {reps} passes: {nbytes} NVFP4 bytes per pass, "
-                      f"{dt:.2f} s in all (numpy elementwise on 1 thread, BLAS on {blas}; "
-                      f"affinity {len(os.sched_getaffinity(0))} cpus)"}
+                      f"gate|up 43008x5376, down 5376x21504; {nbytes} NVFP4 bytes) in {t_layer:.2f} s on one "
+                      f"thread (BLAS limited to 1; affinity {len(os.sched_getaffinity(0))} cpus)",
+            "layer_gemv_s": round(t_layer, 3),
+            "token_ms_scaled": round((N_LAYERS * t_layer + t_head) * 1e3, 1),
+            "token_scaled_from": f"60 x the one-layer GEMV time + the bf16 lm_head GEMV timed on {head_rows} of "
+                                 f"{VOCAB} rows ({t_head / (VOCAB // head_rows):.2f} s) x {VOCAB // head_rows}",
+            "quantize_elements_per_s": round(q_rate, 1),
+            "quantize_sample": f"oracle RTN quantization of the fused q|k|v ({q_elems} elements, 3 segments) in "
+                               f"{t_quant:.2f} s",
+            "load_path_s_scaled": round(24_056_954_880 / q_rate, 1)}
 
 
 def calibrate_copy(dev):
@@ -443,8 +635,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--trials", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-load-path", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the streams, small-M, C0 and C1 workloads")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -453,6 +647,8 @@ def main():
               "(more GPUs would shard rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    state = machine_state()                  # before this process touches the GPU
+    log(f"machine: {state}")
     import nvfp4_weight_only_rtn_amd.attnq as A
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -483,62 +679,67 @@ def main():
 
     graph = None
     if not args.eager:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            model.step()
-        torch.cuda.current_stream().wait_stream(s)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            model.step()
-        graph.replay()
-        torch.cuda.synchronize()
+        graph = graph_of(model.step)
         run = graph.replay
     else:
         run = model.step
     for _ in range(args.warmup):
         run()
-    ms = time_steps(run, args.steps)
+    # trials: each times exactly `steps` replays between synchronizations; the value is the median
+    trial_ms = [time_steps(run, args.steps) for _ in range(max(1, args.trials))]
+    trials = summarize_trials(trial_ms)
+    ms = trials["median_ms"]
     eager_ms = time_steps(model.step, max(3, args.steps // 4))
     bytes_step = model.bytes_per_step()
     tbps = bytes_step / (ms * 1e-3) / 1e12
-    log(f"{'graph' if graph else 'eager'} {ms:.4f} ms/token, eager {eager_ms:.4f} ms/token, {tbps:.3f} TB/s")
+    log(f"{'graph' if graph else 'eager'} {ms:.4f} ms/token (trials {trials['all_ms']}), eager {eager_ms:.4f} ms/token, "
+        f"{tbps:.3f} TB/s")
 
     dom_mean, dom_n = dominant_kernel_timing(model, max(3, args.steps // 2))
     W_gu = model.layers[0]["gate_up"][0]
     dom_bytes = nvfp4_bytes(W_gu.N, W_gu.K, 2)
     achieved = dom_bytes / (dom_mean * 1e-3) / 1e9
 
-    log("timing the chained stream (gate|up epilogue feeds down) and the bf16-attention mix")
-    glu_ms = graph_timing(model.glu_step, args.warmup, args.steps)
-    glu_bytes = model.glu_bytes_per_step()
-    model.build_bf16_attention(dev)
-    mixed_ms = graph_timing(model.mixed_step, args.warmup, args.steps)
-    mixed_bytes = model.mixed_bytes_per_step()
-    model.attn_bf16 = None
-    model.build_lowrank(dev)
-    lr_ms = graph_timing(model.lowrank_step, args.warmup, args.steps)
-    lr_bytes = model.lowrank_bytes_per_step()
-    lr_resident = model.lowrank_resident_bytes()
-    model.lowrank = None
-    torch.cuda.empty_cache()
-    streams = {
-        "glu_chained": {"what": "gate|up GEMV with the gelu-tanh epilogue writing bf16 h, down reading h",
-                        "ms_per_token": round(glu_ms, 5), "bytes_per_token": glu_bytes,
-                        "TBps": round(glu_bytes / (glu_ms * 1e-3) / 1e12, 4)},
-        "bf16_attention": {"what": "q|k|v and o in bf16 (attnq_gemv_bf16), gate|up and down NVFP4, bf16 lm_head",
-                           "ms_per_token": round(mixed_ms, 5), "bytes_per_token": mixed_bytes,
-                           "TBps": round(mixed_bytes / (mixed_ms * 1e-3) / 1e12, 4)},
-        "lowrank_banded": {"what": f"runtime low-rank: {LOWRANK_BANDS} shared NVFP4 blocks in contiguous bands of layers, "
-                                   f"per-layer per-segment s, U, V at rank {LOWRANK_RANK} applied in the GEMV epilogue "
-                                   "(attnq_gemv_nvfp4_lowrank, 2 launches per projection), bf16 lm_head",
-                           "ms_per_token": round(lr_ms, 5), "bytes_per_token": lr_bytes,
-                           "resident_weight_bytes": lr_resident,
-                           "TBps": round(lr_bytes / (lr_ms * 1e-3) / 1e12, 4)},
-    }
-    log(f"streams: {streams}")
+    log("per-projection times and read ceilings")
+    per_proj, ceiling_ms = per_projection_timing(model, max(3, args.steps // 4))
+    log(f"per projection: {per_proj}; token read ceiling {ceiling_ms:.4f} ms")
 
-    small_m = small_m_timing(A, model, max(3, args.steps // 4))
+    streams = small_m = c0 = c1 = None
+    if not args.no_extra:
+        log("timing the chained stream (gate|up epilogue feeds down) and the bf16-attention mix")
+        glu_ms = graph_timing(model.glu_step, args.warmup, args.steps)
+        glu_bytes = model.glu_bytes_per_step()
+        model.build_bf16_attention(dev)
+        mixed_ms = graph_timing(model.mixed_step, args.warmup, args.steps)
+        mixed_bytes = model.mixed_bytes_per_step()
+        model.attn_bf16 = None
+        model.build_lowrank(dev)
+        lr_ms = graph_timing(model.lowrank_step, args.warmup, args.steps)
+        lr_bytes = model.lowrank_bytes_per_step()
+        lr_resident = model.lowrank_resident_bytes()
+        model.lowrank = None
+        torch.cuda.empty_cache()
+        streams = {
+            "glu_chained": {"what": "gate|up GEMV with the gelu-tanh epilogue writing bf16 h, down reading h",
+                            "ms_per_token": round(glu_ms, 5), "bytes_per_token": glu_bytes,
+                            "TBps": round(glu_bytes / (glu_ms * 1e-3) / 1e12, 4)},
+            "bf16_attention": {"what": "q|k|v and o in bf16 (attnq_gemv_bf16), gate|up and down NVFP4, bf16 lm_head",
+                               "ms_per_token": round(mixed_ms, 5), "bytes_per_token": mixed_bytes,
+                               "TBps": round(mixed_bytes / (mixed_ms * 1e-3) / 1e12, 4)},
+            "lowrank_banded": {"what": f"runtime low-rank: {LOWRANK_BANDS} shared NVFP4 blocks in contiguous bands of "
+                                       f"layers, per-layer per-segment s, U, V at rank {LOWRANK_RANK} applied in the GEMV "
+                                       "epilogue (attnq_gemv_nvfp4_lowrank, 2 launches per projection), bf16 lm_head",
+                               "ms_per_token": round(lr_ms, 5), "bytes_per_token": lr_bytes,
+                               "resident_weight_bytes": lr_resident,
+                               "TBps": round(lr_bytes / (lr_ms * 1e-3) / 1e12, 4)},
+        }
+        log(f"streams: {streams}")
+        small_m = small_m_timing(A, model, max(3, args.steps // 4))
+        log(f"small-M: {small_m}")
+        log("single projection 1024x1152 over rotated copies; the 1B-like 26-layer stack")
+        c0 = single_projection_c0(A, dev, args.trials, args.steps)
+        c1 = small_stack_c1(A, dev, args.trials, args.steps)
+        log(f"C0 {c0}; C1 {c1}")
     if args.calibrate_copy:
         calibrate_copy(dev)
 
@@ -556,14 +757,21 @@ def main():
         "dtype": "nvfp4 weights (e2m1 + e4m3 block scales) x bf16 activations, fp32 accumulate",
         "data": "synthetic: seeded device bf16 W0 ~ N(0, 0.02^2) RTN-quantized by the library at load; x ~ N(0, 1)",
         "config": {"workload": "31B-like whole-model weight stream per token: 60 layers x (q|k|v 6144x5376, "
-                               "o 5376x4096, gate|up 43008x5376, down 5376x21504) NVFP4 + bf16 lm_head 262144x5376, batch 1",
+                               "o 5376x4096, gate|up 43008x5376, down 5376x21504 with K split across workgroups) "
+                               "NVFP4 + bf16 lm_head 262144x5376, batch 1",
                    "launches_per_step": 4 * N_LAYERS + 1, "launch": "hipGraph replay" if graph else "stream",
                    "parallelism": "single GPU"},
+        "trials": trials,
         "pct_of_hbm_peak": round(100 * tbps * 1e3 / HBM_PEAK_GBS, 2),
         "ms_per_token": round(ms, 5),
         "ms_per_token_eager": round(eager_ms, 5),
         "bytes_per_token": bytes_step,
         "weight_bytes_per_token": model.weight_bytes_per_step(),
+        "read_ceiling": {"ms_per_token": round(ceiling_ms, 5),
+                         "what": "sum over the token's launches of attnq_read_ceiling over the same weight bytes "
+                                 "(60 x per-layer ceilings + lm_head), each timed back to back over distinct buffers",
+                         "token_frac_of_ceiling": round(ceiling_ms / ms, 4)},
+        "per_projection": per_proj,
         "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4_oneshot<2,1,3,true,8,true,2,0> (fused gate|up 43008x5376)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -571,9 +779,12 @@ def main():
                                  else None),
                      "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_mean * 1e3, 3),
                      "launches_timed": dom_n},
+        "single_projection_1024x1152": c0,
+        "stack_1b_like_26_layers": c1,
         "small_m": small_m,
         "streams": streams,
         "load_path": load,
+        "machine": state,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")

@@ -134,6 +134,31 @@ ATTNQ_API attnq_status attnq_quantize_nvfp4(const attnq_theta* theta, const attn
 ATTNQ_API attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y,
                               attnq_stream stream);
 
+/* The same product y[n] = sum_k x[k] * weight[n][k] with K split across workgroups for long rows
+ * ("Throughput", "The NVFP4 MLP kernels are the least bandwidth-efficient on the step": the down
+ * projection's launch filled too few compute units, and splitting K was the remedy named there).
+ * For rows of 16384 to 49152 elements (K = 21504 for the 31B-like down projection) one kernel runs
+ * the rows in tiles of 16, each tile's K in SK = ceil(K / 4096) slices (4 <= SK <= 12) on separate
+ * workgroups; each workgroup writes its raw partial sums to the workspace, and the workgroup that
+ * arrives last at the tile's ticket adds the SK partials of each row in slice order, applies the
+ * tensor scale and stores y (no workgroup waits on another). The slices are added in a fixed
+ * order, so repeated calls give identical bits. Shorter rows (or rows of more than 49152
+ * elements) run exactly as attnq_gemv_nvfp4 and leave the workspace untouched.
+ * ws: caller-owned device memory of at least attnq_gemv_nvfp4_splitk_workspace(N, K) bytes,
+ * 256-byte aligned. It holds one 832-byte record per tile of 16 rows, at a stride that does not
+ * depend on the weight: a ticket (the first 4 bytes of the record) and the tile's partial sums.
+ * Fill the whole workspace with zeros once after allocating it; every call leaves the tickets
+ * zero again, so one workspace serves any number of calls and any weights whose size query does
+ * not exceed it. Calls that share one workspace must be ordered on one stream.
+ * Errors: as attnq_gemv_nvfp4; ATTNQ_ERR_NULL for a NULL ws that is needed; ATTNQ_ERR_SHAPE for
+ * ws_bytes below the size the shape needs; ATTNQ_ERR_ALIGN for a misaligned ws. */
+ATTNQ_API attnq_status attnq_gemv_nvfp4_splitk(const attnq_nvfp4* W, const uint16_t* x, float* y, void* ws,
+                                     int64_t ws_bytes, attnq_stream stream);
+
+/* Bytes of workspace attnq_gemv_nvfp4_splitk needs for an [N][K] weight (0 when that shape is not
+ * split), or -1 if N < 0 or K is not a positive multiple of 32. Host only, no GPU call. */
+ATTNQ_API int64_t attnq_gemv_nvfp4_splitk_workspace(int32_t N, int32_t K);
+
 /* Activations of the gate|up epilogue (attnq_gemv_nvfp4_glu). The pages do not name the model's
  * activation, so it is a parameter:
  *   GELU_TANH: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)))
@@ -204,6 +229,19 @@ ATTNQ_API attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, 
  * range is ATTNQ_ERR_SHAPE. */
 ATTNQ_API attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, int32_t M,
                                       int32_t ldx, float* Y, int32_t ldy, attnq_stream stream);
+
+/* Measurement aid, not part of the decode path: read a_bytes at a and then b_bytes at b once, as a
+ * plain streaming read (16-byte non-temporal loads, four in flight per lane, 4096 workgroups of 256
+ * threads: a grid-stride walk, or one contiguous stretch per workgroup from 1 GiB up) that writes
+ * nothing in practice. Its duration over a weight's
+ * codes and scales is the practical read ceiling of that weight's GEMV ("Throughput", "What a
+ * decode step is actually made of": a step's byte floor is its weight bytes over the memory
+ * bandwidth). sink: a device uint32 that is written only if the xor of all the data read equals
+ * 0x9E3779B9 (it keeps the loads from being dropped). a, b 16-byte aligned; a_bytes, b_bytes >= 0
+ * and multiples of 16, a_bytes + b_bytes below 63 GiB (b may be NULL when b_bytes == 0). Errors:
+ * ATTNQ_ERR_NULL, ATTNQ_ERR_SHAPE, ATTNQ_ERR_ALIGN, ATTNQ_ERR_HIP. */
+ATTNQ_API attnq_status attnq_read_ceiling(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes,
+                                uint32_t* sink, attnq_stream stream);
 
 /* Static string naming a status code (host only). */
 ATTNQ_API const char* attnq_status_string(attnq_status status);

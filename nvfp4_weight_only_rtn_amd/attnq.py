@@ -42,16 +42,20 @@ _SIGS = {
     "attnq_reconstruct": [ctypes.POINTER(_Theta), _P, _P],
     "attnq_quantize_nvfp4": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), _I, _P],
     "attnq_gemv_nvfp4": [ctypes.POINTER(_NVFP4), _P, _P, _P],
+    "attnq_gemv_nvfp4_splitk": [ctypes.POINTER(_NVFP4), _P, _P, _P, ctypes.c_int64, _P],
     "attnq_gemv_nvfp4_glu": [ctypes.POINTER(_NVFP4), _P, _I, _P, _P],
     "attnq_gemv_nvfp4_lowrank": [ctypes.POINTER(_NVFP4), _P, _P, _P, _I, _P, _P, _P, _P],
     "attnq_gemv_bf16": [_P, _I, _I, _P, _P, _P],
     "attnq_gemm_nvfp4_small_m": [ctypes.POINTER(_NVFP4), _P, _I, _I, _P, _I, _P],
+    "attnq_read_ceiling": [_P, ctypes.c_int64, _P, ctypes.c_int64, _P, _P],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
     getattr(_lib, _name).restype = _S
 _lib.attnq_gemv_nvfp4_lowrank_workspace.argtypes = [_I, _I, _I]
 _lib.attnq_gemv_nvfp4_lowrank_workspace.restype = ctypes.c_int64
+_lib.attnq_gemv_nvfp4_splitk_workspace.argtypes = [_I, _I]
+_lib.attnq_gemv_nvfp4_splitk_workspace.restype = ctypes.c_int64
 _lib.attnq_status_string.argtypes = [_S]
 _lib.attnq_status_string.restype = ctypes.c_char_p
 
@@ -133,6 +137,23 @@ def attnq_gemv_nvfp4(W: NVFP4Weight, x, y, stream=None) -> None:
     _check(_lib.attnq_gemv_nvfp4(ctypes.byref(W.desc()), _ptr(x, 2), _ptr(y, 4), _stream(stream)))
 
 
+def attnq_gemv_nvfp4_splitk_workspace(N: int, K: int) -> int:
+    return int(_lib.attnq_gemv_nvfp4_splitk_workspace(N, K))
+
+
+def splitk_workspace(N: int, K: int, device="cuda") -> torch.Tensor | None:
+    """A zero-filled workspace for attnq_gemv_nvfp4_splitk on [N][K] weights (None if not needed);
+    torch's allocations are 256-byte aligned."""
+    n = attnq_gemv_nvfp4_splitk_workspace(N, K)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def attnq_gemv_nvfp4_splitk(W: NVFP4Weight, x, y, ws, stream=None) -> None:
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.attnq_gemv_nvfp4_splitk(ctypes.byref(W.desc()), _ptr(x, 2), _ptr(y, 4), _ptr(ws), nbytes,
+                                        _stream(stream)))
+
+
 def attnq_gemv_nvfp4_glu(W: NVFP4Weight, x, act: int, h, stream=None) -> None:
     _check(_lib.attnq_gemv_nvfp4_glu(ctypes.byref(W.desc()), _ptr(x, 2), act, _ptr(h, 2), _stream(stream)))
 
@@ -158,6 +179,13 @@ def attnq_gemm_nvfp4_small_m(W: NVFP4Weight, X, Y, stream=None) -> None:
     M = X.shape[0]
     _check(_lib.attnq_gemm_nvfp4_small_m(ctypes.byref(W.desc()), _ptr(X, 2), M, X.stride(0) if M else W.K,
                                          _ptr(Y, 4), Y.stride(0) if M else W.N, _stream(stream)))
+
+
+def attnq_read_ceiling(a, b, sink, stream=None) -> None:
+    """Streaming read of tensors a and b (b may be None), nothing written: the read ceiling."""
+    na = a.numel() * a.element_size()
+    nb = 0 if b is None else b.numel() * b.element_size()
+    _check(_lib.attnq_read_ceiling(_ptr(a), na, _ptr(b), nb, _ptr(sink, 4), _stream(stream)))
 
 
 def raw_library() -> ctypes.CDLL:

@@ -16,7 +16,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattnq.so")
-SOURCES = ["attnq_api.hip", "quantize.hip", "gemv.hip", "gemm_small_m.hip"]
+SOURCES = ["attnq_api.hip", "quantize.hip", "gemv.hip", "gemm_small_m.hip", "read_ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -80,6 +80,26 @@ attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y,
   return from_hip(attnq::launch_gemv_nvfp4(*W, x, y, static_cast<hipStream_t>(stream)));
 }
 
+attnq_status attnq_gemv_nvfp4_splitk(const attnq_nvfp4* W, const uint16_t* x, float* y, void* ws, int64_t ws_bytes,
+                                     attnq_stream stream) {
+  attnq_status st = check_nvfp4(W);
+  if (st != ATTNQ_OK) return st;
+  if (x == nullptr || (y == nullptr && W->N != 0)) return ATTNQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 4)) return ATTNQ_ERR_ALIGN;
+  const int64_t need = attnq::gemv_nvfp4_splitk_workspace_bytes(W->N, W->K);
+  if (need > 0) {
+    if (ws == nullptr) return ATTNQ_ERR_NULL;
+    if (ws_bytes < need) return ATTNQ_ERR_SHAPE;
+    if (!aligned(ws, 256)) return ATTNQ_ERR_ALIGN;
+  }
+  return from_hip(attnq::launch_gemv_nvfp4_splitk(*W, x, y, ws, static_cast<hipStream_t>(stream)));
+}
+
+int64_t attnq_gemv_nvfp4_splitk_workspace(int32_t N, int32_t K) {
+  if (N < 0 || K <= 0 || K % 32 != 0) return -1;
+  return attnq::gemv_nvfp4_splitk_workspace_bytes(N, K);
+}
+
 attnq_status attnq_gemv_nvfp4_glu(const attnq_nvfp4* W, const uint16_t* x, int32_t act, uint16_t* h,
                                   attnq_stream stream) {
   attnq_status st = check_nvfp4(W);
@@ -125,6 +145,15 @@ attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, i
   if ((X == nullptr || Y == nullptr) && M != 0 && W->N != 0) return ATTNQ_ERR_NULL;
   if (!aligned(X, 16) || !aligned(Y, 4)) return ATTNQ_ERR_ALIGN;
   return from_hip(attnq::launch_gemm_nvfp4_small_m(*W, X, M, ldx, Y, ldy, static_cast<hipStream_t>(stream)));
+}
+
+attnq_status attnq_read_ceiling(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes, uint32_t* sink,
+                                attnq_stream stream) {
+  if (a_bytes < 0 || b_bytes < 0 || a_bytes % 16 != 0 || b_bytes % 16 != 0) return ATTNQ_ERR_SHAPE;
+  if (a_bytes + b_bytes >= (int64_t{63} << 30)) return ATTNQ_ERR_SHAPE;   // 32-bit piece indices
+  if ((a == nullptr && a_bytes > 0) || (b == nullptr && b_bytes > 0) || sink == nullptr) return ATTNQ_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sink, 4)) return ATTNQ_ERR_ALIGN;
+  return from_hip(attnq::launch_read_ceiling(a, a_bytes, b, b_bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
 const char* attnq_status_string(attnq_status status) {

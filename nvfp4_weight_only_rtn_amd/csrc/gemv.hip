@@ -410,6 +410,125 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_oneshot(const uint8_t
   }
 }
 
+// Cross-workgroup K split for long rows (the down projection, 5376 x 21504: rows too few for the
+// batch-1 kernels to fill the chip with whole rows). Workgroup b takes row tile b / SK (WAVES x R
+// rows, R per wave) and K slice b % SK: it stages its slice of x in LDS and runs the one-shot walk
+// over it (every code and scale load of the slice issued at once, x loaded ahead of them), then
+// writes the tile's raw partial sums into the tile's record. The workgroup that arrives last at the
+// tile's ticket adds the SK partials of each row in slice order (so the bits do not depend on the
+// arrival order), applies the tensor scale, stores y and returns the ticket to zero. Nothing waits:
+// a workgroup either finishes the tile or leaves.
+//
+// Publication without cache maintenance: an agent-scope release/acquire fence pair writes back and
+// invalidates an XCD's whole L2 on this part, and with it the kernel measured 71.5 us instead of
+// 14.6 us. So the partials are written and read with agent-scope atomic stores and loads, which go
+// through the caches to the coherent level; a workgroup-scope fence plus a wait for the vector-memory
+// counter orders the partial stores before the ticket increment, and the same pair after the
+// increment keeps the partial loads behind it.
+//
+// Workspace: one record per row tile at a fixed stride, so that weights of any shape can take
+// turns on one workspace: the ticket in the record's first 64-byte slot, then one slot per K slice
+// with the tile's 16 partial sums (fp32).
+constexpr int kSplitSlotBytes = 64;
+constexpr int kSplitMaxSlices = 12;
+constexpr int kSplitRecordBytes = kSplitSlotBytes * (1 + kSplitMaxSlices);
+
+__device__ __forceinline__ void wait_vector_memory() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0); expcnt and lgkmcnt left at their maxima
+}
+
+template <int R, int S, int WAVES, int XI, int SK>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_splitk(const uint8_t* __restrict__ codes,
+                                                                  const uint8_t* __restrict__ scales,
+                                                                  const float* __restrict__ tensor_scale, SegTable segs,
+                                                                  const uint16_t* __restrict__ x, float* __restrict__ y,
+                                                                  int N, int K, uint8_t* ws) {
+  constexpr int kPitch = S * 64 + 4;          // padded as in the one-shot kernel (conflict-free staging)
+  constexpr int kTileRows = WAVES * R;
+  static_assert(kTileRows * 4 == kSplitSlotBytes && SK <= kSplitMaxSlices, "a slice's partials fill one slot");
+  __shared__ u32x4 xs[4 * kPitch];
+  __shared__ float red[kTileRows];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x / SK, ks = blockIdx.x - tile * SK;
+  const int row0 = tile * kTileRows + wave * R;
+  const int cpr = K >> 5;
+  const int slice = (cpr + SK - 1) / SK;
+  const int c_begin = ks * slice;                       // the launcher guarantees c_begin < cpr
+  const int nck = min(cpr, c_begin + slice) - c_begin;  // chunks of this slice, 1 .. S * 64
+  const u32x4* xg = reinterpret_cast<const u32x4*>(x) + 4 * c_begin;
+
+  u32x4 xst[XI];
+#pragma unroll
+  for (int j = 0; j < XI; ++j) xst[j] = xg[min((int)threadIdx.x + j * 64 * WAVES, 4 * nck - 1)];
+  uint32_t crow[R], srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t row = (uint32_t)min(row0 + r, N - 1);     // rows past N load row N-1, result discarded
+    crow[r] = row * (uint32_t)(K >> 1);
+    srow[r] = row * (uint32_t)(K >> 4);
+  }
+  u32x4 cv[S][R];
+  uint32_t sv[S][R];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint32_t c = (uint32_t)(c_begin + min(s * 64 + lane, nck - 1));   // clamped into the slice
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      cv[s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + (crow[r] + 16u * c)));
+      sv[s][r] = *reinterpret_cast<const uint16_t*>(scales + (srow[r] + 2u * c));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int i = threadIdx.x + j * 64 * WAVES;
+    if (i < 4 * nck) xs[(i & 3) * kPitch + (i >> 2)] = xst[j];
+  }
+  __syncthreads();
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = s * 64 + lane;
+    if (c < nck) {
+      const u32x4 x0 = xs[c], x1 = xs[kPitch + c], x2 = xs[2 * kPitch + c], x3 = xs[3 * kPitch + c];
+      const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                               x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = chunk_dot(cv[s][r], sv[s][r], xw, acc[r]);
+    }
+  }
+  wave_sums<R>(acc);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[wave * R + r] = acc[r];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // wave 0 publishes the tile's partials in the tile's record and takes its ticket
+  const int row = tile * kTileRows + lane;
+  const bool mine = lane < kTileRows && row < N;
+  uint32_t* ticket = reinterpret_cast<uint32_t*>(ws + (size_t)tile * kSplitRecordBytes);
+  float* part = reinterpret_cast<float*>(ws + (size_t)tile * kSplitRecordBytes + kSplitSlotBytes) + lane;
+  if (mine) __hip_atomic_store(part + ks * kTileRows, red[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  wait_vector_memory();                                    // the partial stores have completed
+  uint32_t arrived = 0u;
+  if (lane == 0) arrived = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__builtin_amdgcn_readfirstlane(arrived) != SK - 1) return;       // lane 0's count, wave-uniform
+  wait_vector_memory();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // the partial loads stay behind the ticket
+  if (mine) {
+    float v = __hip_atomic_load(part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k2 = 1; k2 < SK; ++k2)
+      v += __hip_atomic_load(part + k2 * kTileRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    y[row] = v * tensor_scale[segment_of(segs, row)];
+  }
+  if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Small-M product for M = 1 .. 4 tokens on the batch-1 walk (rows of at most S x 64 chunks): the
 // weight loads are the one-shot kernel's (each wave load instruction 1 KiB of one row, all of a
 // lane's loads issued at once), every token's x is staged in LDS as [token][quarter][chunk], and a
@@ -803,6 +922,32 @@ bool launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, in
   return true;
 }
 
+// Split-K shape: slices of at most 2 x 64 chunks (4096 elements) on 8 waves of two rows each, SK =
+// ceil(chunks / 128) slices (4 <= SK <= 12), every slice non-empty; rows of fewer than 512 chunks
+// (16384 elements) or more than 1536 (49152) are not split. For the down projection (672 chunks)
+// that is 6 slices of 112 chunks, 2016 workgroups: in the token stream this measured 14.0 us against
+// 14.2-14.9 us for 7 or 8 slices of two steps, 14.8 us for 4 slices of three steps, 15.6 us for 3
+// of four, 14.5-15.0 us with four rows per wave, 15.3-17.0 us with one step per slice (11 or 12
+// slices) and 17.0-17.4 us with one row per wave (16 waves).
+constexpr int kSplitRows = 16;        // a tile: 8 waves x 2 rows
+constexpr int kSplitS = 2, kSplitR = 2, kSplitWaves = kSplitRows / kSplitR;
+int splitk_slices(int K) {
+  const int cpr = K / 32;
+  if (cpr < 512) return 0;
+  const int sk = (cpr + kSplitS * 64 - 1) / (kSplitS * 64);
+  if (sk < 2 || sk > kSplitMaxSlices) return 0;
+  const int slice = (cpr + sk - 1) / sk;
+  return (slice <= kSplitS * 64 && (sk - 1) * slice < cpr) ? sk : 0;
+}
+
+template <int SK>
+void launch_splitk_sk(const attnq_nvfp4& W, const uint16_t* x, float* y, uint8_t* ws, hipStream_t stream) {
+  const unsigned tiles = (unsigned)((W.N + kSplitRows - 1) / kSplitRows);
+  constexpr int kXI = (4 * kSplitS * 64 + 64 * kSplitWaves - 1) / (64 * kSplitWaves);   // x pieces per thread
+  k_gemv_nvfp4_splitk<kSplitR, kSplitS, kSplitWaves, kXI, SK><<<tiles * SK, 64 * kSplitWaves, 0, stream>>>(
+      W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K, ws);
+}
+
 }  // namespace
 
 // Launch table (timed per shape on MI355X, 31B-like shapes streamed cold, then A/B inside the
@@ -828,6 +973,33 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
   else
     launch_nvfp4_loop<2, 2>(W, x, y, stream);
   return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+// Workspace of the split-K GEMV: one record per row tile (0 for shapes that are not split).
+int64_t gemv_nvfp4_splitk_workspace_bytes(int N, int K) {
+  const int sk = splitk_slices(K);
+  if (sk == 0 || N == 0) return 0;
+  return (int64_t)((N + kSplitRows - 1) / kSplitRows) * kSplitRecordBytes;
+}
+
+hipError_t launch_gemv_nvfp4_splitk(const attnq_nvfp4& W, const uint16_t* x, float* y, void* ws, hipStream_t stream) {
+  const int sk = splitk_slices(W.K);
+  if (W.N == 0) return hipSuccess;
+  if (sk == 0) return launch_gemv_nvfp4(W, x, y, stream);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  switch (sk) {
+    case 4: launch_splitk_sk<4>(W, x, y, w, stream); break;
+    case 5: launch_splitk_sk<5>(W, x, y, w, stream); break;
+    case 6: launch_splitk_sk<6>(W, x, y, w, stream); break;
+    case 7: launch_splitk_sk<7>(W, x, y, w, stream); break;
+    case 8: launch_splitk_sk<8>(W, x, y, w, stream); break;
+    case 9: launch_splitk_sk<9>(W, x, y, w, stream); break;
+    case 10: launch_splitk_sk<10>(W, x, y, w, stream); break;
+    case 11: launch_splitk_sk<11>(W, x, y, w, stream); break;
+    case 12: launch_splitk_sk<12>(W, x, y, w, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // Small-M on the batch-1 walk: M = 1 .. 4 tokens and rows of at most 192 chunks, in the batch-1

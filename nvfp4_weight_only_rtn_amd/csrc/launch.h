@@ -12,10 +12,17 @@ hipError_t launch_reconstruct(const attnq_theta& theta, uint16_t* W_eff, hipStre
 hipError_t launch_quantize(const attnq_theta& theta, uint8_t* codes, uint8_t* scales, float* tensor_scale,
                            hipStream_t stream);
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream);
+// K split across workgroups for rows of 16384 elements or more (other shapes: launch_gemv_nvfp4);
+// ws holds the tickets (zero on entry, zero again on exit) and the partial sums
+hipError_t launch_gemv_nvfp4_splitk(const attnq_nvfp4& W, const uint16_t* x, float* y, void* ws, hipStream_t stream);
+int64_t gemv_nvfp4_splitk_workspace_bytes(int N, int K);
 hipError_t launch_gemv_nvfp4_glu(const attnq_nvfp4& W, const uint16_t* x, int act, uint16_t* h, hipStream_t stream);
 hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, const uint16_t* U, const uint16_t* V,
                                      int r, const uint16_t* x, float* ws, float* y, hipStream_t stream);
 int64_t lowrank_workspace_floats(int K, int n_seg, int r);
+// streaming read of two byte ranges (multiples of 16 bytes), nothing written: the read ceiling
+hipError_t launch_read_ceiling(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes, uint32_t* sink,
+                               hipStream_t stream);
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_gemm_nvfp4_small_m(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
                                      hipStream_t stream);

@@ -29,8 +29,8 @@ def test_header_declares_every_call():
     names = _declared_functions()
     for n in ["attnq_reconstruct", "attnq_quantize_nvfp4", "attnq_gemv_nvfp4", "attnq_gemv_bf16",
               "attnq_gemm_nvfp4_small_m", "attnq_gemv_nvfp4_glu", "attnq_gemv_nvfp4_lowrank",
-              "attnq_gemv_nvfp4_lowrank_workspace",
-              "attnq_status_string"]:
+              "attnq_gemv_nvfp4_lowrank_workspace", "attnq_gemv_nvfp4_splitk",
+              "attnq_gemv_nvfp4_splitk_workspace", "attnq_read_ceiling", "attnq_status_string"]:
         assert n in names
 
 
@@ -52,6 +52,22 @@ def test_lowrank_workspace_sizes():
     assert ws(96, 2, 3) == 2 * 1 * 3               # 5461 rows per chunk
     assert ws(32, 1, 1) == 1
     for bad in [(0, 1, 4), (40, 1, 4), (64, 0, 4), (64, 5, 4), (64, 1, 65), (64, 1, -1)]:
+        assert ws(*bad) == -1
+
+
+def test_splitk_workspace_sizes():
+    ws = A.attnq_gemv_nvfp4_splitk_workspace
+    # rows under 16384 elements are not split
+    assert ws(5376, 4096) == 0 and ws(43008, 5376) == 0 and ws(100, 16384 - 32) == 0
+    # one 832-byte record (a ticket slot and 12 partial slots of 64 B) per tile of 16 rows, for every
+    # split shape: down 5376 x 21504 (672 chunks -> 6 slices of 112) has 336 tiles
+    assert ws(5376, 21504) == 336 * 832
+    assert ws(1, 16384) == 832                         # 512 chunks -> 4 slices of 128
+    assert ws(17, 24576) == 2 * 832                    # 768 chunks -> 6 slices of 128
+    assert ws(100, 49152) == 7 * 832                   # 1536 chunks -> 12 slices of 128
+    assert ws(100, 49152 + 32) == 0                    # would need 13 slices: not split
+    assert ws(0, 21504) == 0
+    for bad in [(-1, 21504), (64, 0), (64, 48)]:
         assert ws(*bad) == -1
 
 
@@ -173,6 +189,23 @@ def test_gemv_and_gemm_validation():
     assert lr(ctypes.byref(nv), FAKE, FAKE + 1, FAKE, 4, FAKE, FAKE, FAKE, None) == 3    # U 2-byte
     assert lr(ctypes.byref(nv), FAKE, FAKE, FAKE + 8, 4, FAKE, FAKE, FAKE, None) == 3    # V 16-byte
     assert lr(ctypes.byref(_nv(K=16)), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 2
+    sk = lib.attnq_gemv_nvfp4_splitk
+    down = _nv(N=64, K=21504)
+    need = A.attnq_gemv_nvfp4_splitk_workspace(64, 21504)
+    assert sk(ctypes.byref(down), FAKE, FAKE, None, need, None) == 1             # workspace needed
+    assert sk(ctypes.byref(down), FAKE, FAKE, FAKE, need - 1, None) == 2         # too small
+    assert sk(ctypes.byref(down), FAKE, FAKE, FAKE + 128, need, None) == 3       # 256-byte alignment
+    assert sk(ctypes.byref(down), None, FAKE, FAKE, need, None) == 1
+    assert sk(ctypes.byref(down), FAKE + 8, FAKE, FAKE, need, None) == 3
+    assert sk(ctypes.byref(_nv(K=16)), FAKE, FAKE, FAKE, need, None) == 2
+    assert sk(ctypes.byref(_nv(layout=1)), FAKE, FAKE, FAKE, need, None) == 5
+    rc = lib.attnq_read_ceiling
+    assert rc(FAKE, 24, None, 0, FAKE, None) == 2                                 # not a multiple of 16
+    assert rc(FAKE, -16, None, 0, FAKE, None) == 2
+    assert rc(FAKE, 64, None, 16, FAKE, None) == 1                                # b missing
+    assert rc(FAKE, 64, None, 0, None, None) == 1                                 # sink missing
+    assert rc(FAKE + 8, 64, None, 0, FAKE, None) == 3
+    assert rc(FAKE, 63 << 30, None, 0, FAKE, None) == 2                          # 32-bit piece indices
     g = lib.attnq_gemm_nvfp4_small_m
     assert g(ctypes.byref(nv), FAKE, 17, 64, FAKE, 64, None) == 2                 # M > 16
     assert g(ctypes.byref(nv), FAKE, 4, 32, FAKE, 64, None) == 2                  # ldx < K

@@ -123,3 +123,45 @@ def test_rank16_load_path_full_size(A, name):
                for i, n in enumerate(seg_rows)]
     x = inputs.activation_bf16(1, K, 4, 1, list(SHAPES).index(name))
     _check_projection(A, f"rank16 {name}", bundles, seg_rows, K, x)
+
+
+def _abs_dot_chunked(c, s, t, x, seg_end, chunk=4096):
+    """abs_dot over every row, a row chunk at a time (bounded host memory)."""
+    out = np.empty(c.shape[0], dtype=np.float64)
+    for a in range(0, c.shape[0], chunk):
+        rows = np.arange(a, min(a + chunk, c.shape[0]))
+        out[rows] = O.abs_dot(c, s, t, x, seg_end, rows=rows)[0]
+    return out
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_every_row_at_full_size(A, name):
+    """The dominant launch class (the fused gate|up, 43008 x 5376) and the down projection, each
+    quantized by the oracle in full: packed bytes bit-exact on every row, and y on every row within
+    the fp32 bounds -- gate|up through attnq_gemv_nvfp4, down through both attnq_gemv_nvfp4 and the
+    split-K call."""
+    seg_rows, K = SHAPES[name]
+    bundles = [inputs.theta_bundle(n, K, 0, cfg=2, layer=5, proj=10 * list(SHAPES).index(name) + i, passthrough=True)
+               for i, n in enumerate(seg_rows)]
+    x = inputs.activation_bf16(1, K, 2, 5, list(SHAPES).index(name))
+    say(f"every row {name}: quantize")
+    W, seg_end = gpu_quantize(A, bundles, K)
+    c, s, t, _ = oracle_quantize(bundles)
+    assert_same_bits(host(W.codes), c, f"{name} codes")
+    assert_same_bits(host(W.scales), s, f"{name} scales")
+    assert_same_bits(host(W.tensor_scale).view(np.uint32), t.view(np.uint32), f"{name} tensor scales")
+    y_ref = O.gemv_nvfp4(c, s, t, x, seg_end, chunk_rows=2048)
+    absdot = _abs_dot_chunked(c, s, t, x, seg_end)
+    xd = dev(x.reshape(-1))
+    say(f"every row {name}: gemv")
+    y = torch.full((W.N,), np.nan, dtype=torch.float32, device="cuda")
+    A.attnq_gemv_nvfp4(W, xd, y)
+    torch.cuda.synchronize()
+    assert_close_products(host(y), y_ref, absdot, f"{name} gemv, every row")
+    if name == "down":
+        say("every row down: split-K gemv")
+        ws = A.splitk_workspace(W.N, K)
+        y.fill_(float("nan"))
+        A.attnq_gemv_nvfp4_splitk(W, xd, y, ws)
+        torch.cuda.synchronize()
+        assert_close_products(host(y), y_ref, absdot, "down split-K gemv, every row")
