@@ -18,8 +18,9 @@
  *
  * Conventions shared by every call:
  *   - Memory: every array argument is DEVICE memory owned by the caller; descriptor structs
- *     are HOST memory read during the call only. The library allocates nothing and keeps no
- *     mutable global state, so calls from several host threads are safe.
+ *     are HOST memory read during the call only. The library allocates nothing and, apart from
+ *     the scratch array of attnq_gemv_nvfp4_splitk_noalloc, keeps no mutable global state, so
+ *     calls from several host threads are safe.
  *   - Asynchrony: each call validates its arguments on the host, enqueues its kernels on
  *     `stream` (a hipStream_t; NULL is the default stream) and returns. It never
  *     synchronizes, copies to or from the host, or reads device data on the host.
@@ -154,6 +155,19 @@ ATTNQ_API attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x,
  * ws_bytes below the size the shape needs; ATTNQ_ERR_ALIGN for a misaligned ws. */
 ATTNQ_API attnq_status attnq_gemv_nvfp4_splitk(const attnq_nvfp4* W, const uint16_t* x, float* y, void* ws,
                                      int64_t ws_bytes, attnq_stream stream);
+
+/* attnq_gemv_nvfp4_splitk without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The tile records live in a 1 MiB array inside the library, one per GPU,
+ * held until the process ends; the first call on a device looks up that device's copy and clears
+ * it with a kernel on `stream`. Shapes that need more than 1 MiB of records (more than 20160 rows,
+ * for split rows) return ATTNQ_ERR_SHAPE; shapes that are not split run as attnq_gemv_nvfp4. The
+ * results equal attnq_gemv_nvfp4_splitk's bit for bit. Every call on one GPU shares that GPU's
+ * array (each call leaves its tickets zero), so calls that overlap on one GPU -- on different
+ * streams, or from several host threads without stream ordering -- race and must not be made.
+ * `stream` must belong to the current device. Errors: as attnq_gemv_nvfp4_splitk. */
+ATTNQ_API attnq_status attnq_gemv_nvfp4_splitk_noalloc(const attnq_nvfp4* W, const uint16_t* x, float* y,
+                                             attnq_stream stream);
 
 /* Bytes of workspace attnq_gemv_nvfp4_splitk needs for an [N][K] weight (0 when that shape is not
  * split), or -1 if N < 0 or K is not a positive multiple of 32. Host only, no GPU call. */

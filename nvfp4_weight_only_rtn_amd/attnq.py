@@ -43,6 +43,7 @@ _SIGS = {
     "attnq_quantize_nvfp4": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), _I, _P],
     "attnq_gemv_nvfp4": [ctypes.POINTER(_NVFP4), _P, _P, _P],
     "attnq_gemv_nvfp4_splitk": [ctypes.POINTER(_NVFP4), _P, _P, _P, ctypes.c_int64, _P],
+    "attnq_gemv_nvfp4_splitk_noalloc": [ctypes.POINTER(_NVFP4), _P, _P, _P],
     "attnq_gemv_nvfp4_glu": [ctypes.POINTER(_NVFP4), _P, _I, _P, _P],
     "attnq_gemv_nvfp4_lowrank": [ctypes.POINTER(_NVFP4), _P, _P, _P, _I, _P, _P, _P, _P],
     "attnq_gemv_bf16": [_P, _I, _I, _P, _P, _P],
@@ -152,6 +153,10 @@ def attnq_gemv_nvfp4_splitk(W: NVFP4Weight, x, y, ws, stream=None) -> None:
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.attnq_gemv_nvfp4_splitk(ctypes.byref(W.desc()), _ptr(x, 2), _ptr(y, 4), _ptr(ws), nbytes,
                                         _stream(stream)))
+
+
+def attnq_gemv_nvfp4_splitk_noalloc(W: NVFP4Weight, x, y, stream=None) -> None:
+    _check(_lib.attnq_gemv_nvfp4_splitk_noalloc(ctypes.byref(W.desc()), _ptr(x, 2), _ptr(y, 4), _stream(stream)))
 
 
 def attnq_gemv_nvfp4_glu(W: NVFP4Weight, x, act: int, h, stream=None) -> None:

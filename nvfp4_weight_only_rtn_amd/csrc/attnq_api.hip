@@ -95,6 +95,16 @@ attnq_status attnq_gemv_nvfp4_splitk(const attnq_nvfp4* W, const uint16_t* x, fl
   return from_hip(attnq::launch_gemv_nvfp4_splitk(*W, x, y, ws, static_cast<hipStream_t>(stream)));
 }
 
+attnq_status attnq_gemv_nvfp4_splitk_noalloc(const attnq_nvfp4* W, const uint16_t* x, float* y, attnq_stream stream) {
+  attnq_status st = check_nvfp4(W);
+  if (st != ATTNQ_OK) return st;
+  if (x == nullptr || (y == nullptr && W->N != 0)) return ATTNQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 4)) return ATTNQ_ERR_ALIGN;
+  if (attnq::gemv_nvfp4_splitk_workspace_bytes(W->N, W->K) > attnq::gemv_nvfp4_splitk_noalloc_max_bytes())
+    return ATTNQ_ERR_SHAPE;
+  return from_hip(attnq::launch_gemv_nvfp4_splitk_noalloc(*W, x, y, static_cast<hipStream_t>(stream)));
+}
+
 int64_t attnq_gemv_nvfp4_splitk_workspace(int32_t N, int32_t K) {
   if (N < 0 || K <= 0 || K % 32 != 0) return -1;
   return attnq::gemv_nvfp4_splitk_workspace_bytes(N, K);

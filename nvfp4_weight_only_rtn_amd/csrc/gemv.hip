@@ -14,6 +14,8 @@
 // v_cvt_scalef32_pk_bf16_fp4 (two fp4 -> two bf16, exact, scale 1) feeding v_dot2c_f32_bf16
 // into a per-block fp32 partial, which is multiplied by its E4M3 scale once per block. Wave
 // partials are reduced with DPP; with a K split, the waves of a workgroup meet in LDS.
+#include <mutex>
+
 #include "attnq_device.h"
 #include "launch.h"
 
@@ -529,6 +531,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_splitk(const uint8_t*
   if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__global__ __launch_bounds__(256) void k_clear_words(uint32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
 // Small-M product for M = 1 .. 4 tokens on the batch-1 walk (rows of at most S x 64 chunks): the
 // weight loads are the one-shot kernel's (each wave load instruction 1 KiB of one row, all of a
 // lane's loads issued at once), every token's x is staged in LDS as [token][quarter][chunk], and a
@@ -1000,6 +1006,49 @@ hipError_t launch_gemv_nvfp4_splitk(const attnq_nvfp4& W, const uint16_t* x, flo
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// The allocation-free split-K entry point keeps its tile records in this device array: 1 MiB, 1260
+// records, so weights of up to 20160 rows. Each GPU the library runs on holds its own copy until the
+// process ends. Host code never names the array in a launch or a copy (its host-side name is not a
+// device address): at a device's first call its address is taken once with hipGetSymbolAddress,
+// with that device current, and kept per device; the array is cleared by a kernel then.
+constexpr int64_t kScratchBytes = int64_t{1} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_of_current_device(hipStream_t stream, uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    k_clear_words<<<256, 256, 0, stream>>>(static_cast<uint32_t*>(p), (int)(kScratchBytes / 4));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+int64_t gemv_nvfp4_splitk_noalloc_max_bytes() { return kScratchBytes; }
+
+hipError_t launch_gemv_nvfp4_splitk_noalloc(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream) {
+  if (gemv_nvfp4_splitk_workspace_bytes(W.N, W.K) == 0) return launch_gemv_nvfp4(W, x, y, stream);
+  uint8_t* ws = nullptr;
+  const hipError_t e = scratch_of_current_device(stream, &ws);
+  if (e != hipSuccess) return e;
+  return launch_gemv_nvfp4_splitk(W, x, y, ws, stream);
 }
 
 // Small-M on the batch-1 walk: M = 1 .. 4 tokens and rows of at most 192 chunks, in the batch-1

@@ -16,6 +16,9 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
 // ws holds the tickets (zero on entry, zero again on exit) and the partial sums
 hipError_t launch_gemv_nvfp4_splitk(const attnq_nvfp4& W, const uint16_t* x, float* y, void* ws, hipStream_t stream);
 int64_t gemv_nvfp4_splitk_workspace_bytes(int N, int K);
+// the same with the library's own per-device scratch (no allocation); the caller checks the size
+hipError_t launch_gemv_nvfp4_splitk_noalloc(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream);
+int64_t gemv_nvfp4_splitk_noalloc_max_bytes();
 hipError_t launch_gemv_nvfp4_glu(const attnq_nvfp4& W, const uint16_t* x, int act, uint16_t* h, hipStream_t stream);
 hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, const uint16_t* U, const uint16_t* V,
                                      int r, const uint16_t* x, float* ws, float* y, hipStream_t stream);

@@ -30,7 +30,8 @@ def test_header_declares_every_call():
     for n in ["attnq_reconstruct", "attnq_quantize_nvfp4", "attnq_gemv_nvfp4", "attnq_gemv_bf16",
               "attnq_gemm_nvfp4_small_m", "attnq_gemv_nvfp4_glu", "attnq_gemv_nvfp4_lowrank",
               "attnq_gemv_nvfp4_lowrank_workspace", "attnq_gemv_nvfp4_splitk",
-              "attnq_gemv_nvfp4_splitk_workspace", "attnq_read_ceiling", "attnq_status_string"]:
+              "attnq_gemv_nvfp4_splitk_workspace", "attnq_gemv_nvfp4_splitk_noalloc", "attnq_read_ceiling",
+              "attnq_status_string"]:
         assert n in names
 
 
@@ -199,6 +200,12 @@ def test_gemv_and_gemm_validation():
     assert sk(ctypes.byref(down), FAKE + 8, FAKE, FAKE, need, None) == 3
     assert sk(ctypes.byref(_nv(K=16)), FAKE, FAKE, FAKE, need, None) == 2
     assert sk(ctypes.byref(_nv(layout=1)), FAKE, FAKE, FAKE, need, None) == 5
+    na = lib.attnq_gemv_nvfp4_splitk_noalloc
+    assert na(ctypes.byref(_nv(N=20176, K=16384)), FAKE, FAKE, None) == 2       # 1261 tiles > 1 MiB of records
+    assert na(ctypes.byref(_nv(N=20160, K=49152 + 32)), FAKE, FAKE + 2, None) == 3   # unsplit shape: checks still run
+    assert na(ctypes.byref(down), None, FAKE, None) == 1
+    assert na(ctypes.byref(down), FAKE + 8, FAKE, None) == 3
+    assert na(ctypes.byref(_nv(layout=1)), FAKE, FAKE, None) == 5
     rc = lib.attnq_read_ceiling
     assert rc(FAKE, 24, None, 0, FAKE, None) == 2                                 # not a multiple of 16
     assert rc(FAKE, -16, None, 0, FAKE, None) == 2
