@@ -58,7 +58,7 @@ LOWRANK_RANK = 16
 # HBM traffic of one fused gate|up launch from the FETCH_SIZE / WRITE_SIZE passes recorded in
 # profiles/gemv_nvfp4_31b_token_traffic.md (FETCH scaled x1.9999, WRITE x1.0 by a 1 GiB copy).
 # Valid only for the kernel code it was measured on: reported as null once that changes.
-GATE_UP_TRAFFIC = {"sources_sha256_16": "f47580bdeb0b1039", "bytes": 130367486}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "7f9e63ce0fadeb2c", "bytes": 130371828}
 
 
 def gemv_sources_hash() -> str:
@@ -396,13 +396,20 @@ def summarize_trials(ms: list) -> dict:
             "max_ms": round(v[-1], 5), "all_ms": [round(t, 5) for t in ms]}
 
 
+EAGER = False          # --eager: every timing launches on the stream (counter passes see each dispatch)
+
+
 def per_launch_us(fn_list, reps: int) -> float:
     """Average duration of back-to-back launches: the launches of `fn_list` (each item one launch on
     distinct buffers) captured once as a hipGraph, replayed `reps` times between two HIP events on
-    the stream the graph runs on -- the conditions of the token stream."""
+    the stream the graph runs on -- the conditions of the token stream (with --eager, launched on the
+    stream instead)."""
     def run():
         for f in fn_list:
             f()
+    if EAGER:
+        run()
+        return time_steps(run, reps) * 1e3 / len(fn_list)
     g = graph_of(run)
     ms = time_steps(g.replay, reps)
     del g
@@ -647,6 +654,8 @@ def main():
               "(more GPUs would shard rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    global EAGER
+    EAGER = args.eager
     state = machine_state()                  # before this process touches the GPU
     log(f"machine: {state}")
     import nvfp4_weight_only_rtn_amd.attnq as A
