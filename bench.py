@@ -332,39 +332,31 @@ def load_path_timing(A, dev, model: Model, reps: int = 1):
 
 
 def small_m_timing(A, model: Model, steps: int):
-    """M = 4 (gamma 3 + 1) and M = 8 verify products over one layer's four projections."""
+    """M = 4 (gamma 3 + 1) and M = 8 verify products over one 31B-like layer's four projections through
+    attnq_gemm_nvfp4_small_m_splitk (one workspace for all of them), timed cold by walking 8 distinct
+    layers in a hipGraph; per-projection figures are the same launches class by class."""
     out = {}
-    lay = model.layers[0]
     for M in (4, 8):
-        bufs = []
-        nbytes = 0
-        flops = 0
+        need = max(A.attnq_gemm_nvfp4_small_m_splitk_workspace(model.layers[0][n][0].N, model.layers[0][n][4], M)
+                   for n in PROJ_NAMES)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        nbytes = flops = 0
+        per = {}
+        all_fns = []
         for name in PROJ_NAMES:
-            W, _, _, segs, K = lay[name]
+            W0, _, _, segs, K = model.layers[0][name]
             X = torch.randn((M, K), device="cuda").to(torch.bfloat16)
-            Y = torch.empty((M, W.N), dtype=torch.float32, device="cuda")
-            bufs.append((W, X, Y))
-            nbytes += W.nbytes + 2 * M * K + 4 * M * W.N
-            flops += 2 * M * W.N * K
-
-        def run():
-            for (W, X, Y) in bufs:
-                A.attnq_gemm_nvfp4_small_m(W, X, Y)
-        run()
-        # one layer (226 MB) fits the 256 MB last-level cache; time it cold by walking 8 layers
-        bufs_all = []
-        for L in range(8):
-            for name in PROJ_NAMES:
-                W, _, _, segs, K = model.layers[L][name]
-                bufs_all.append((W, bufs[PROJ_NAMES.index(name)][1], bufs[PROJ_NAMES.index(name)][2]))
-
-        def run8():
-            for (W, X, Y) in bufs_all:
-                A.attnq_gemm_nvfp4_small_m(W, X, Y)
-        run8()
-        ms = time_steps(run8, steps) / 8
-        out[f"M{M}"] = {"us_per_layer": round(ms * 1e3, 2), "TBps": round(nbytes / (ms * 1e-3) / 1e12, 3),
-                        "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2)}
+            Y = torch.empty((M, W0.N), dtype=torch.float32, device="cuda")
+            nbytes += W0.nbytes + 2 * M * K + 4 * M * W0.N
+            flops += 2 * M * W0.N * K
+            fns = [lambda W=model.layers[L][name][0], X=X, Y=Y: A.attnq_gemm_nvfp4_small_m_splitk(W, X, Y, ws)
+                   for L in range(8)]
+            per[name] = round(per_launch_us(fns, steps), 2)
+            all_fns.append(fns)
+        layer_fns = [f for L in range(8) for f in (all_fns[p][L] for p in range(len(PROJ_NAMES)))]
+        us = per_launch_us(layer_fns, steps) * len(PROJ_NAMES)
+        out[f"M{M}"] = {"us_per_layer": round(us, 2), "TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
+                        "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2), "per_projection_us": per}
     return out
 
 

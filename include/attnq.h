@@ -244,6 +244,29 @@ ATTNQ_API attnq_status attnq_gemv_bf16(const uint16_t* W, int32_t N, int32_t K, 
 ATTNQ_API attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, int32_t M,
                                       int32_t ldx, float* Y, int32_t ldy, attnq_stream stream);
 
+/* The small-M product of attnq_gemm_nvfp4_small_m with K cut into slices on separate workgroups
+ * ("Throughput", "Speculative decoding": the verify pass at gamma + 1 = 4 tokens; batch 8): for
+ * rows of more than 6144 elements, and for weights of at least 16384 rows at M > 4 (the down and
+ * fused gate|up projections), one kernel reads each slice's weights the
+ * way the batch-1 GEMV does (all of a slice's loads issued at once), turns them into matrix-core
+ * operands through LDS and writes the slice's raw partial sums to the workspace; a second kernel,
+ * in stream order, adds the slices in slice order, applies the tensor scale and stores Y. Repeated
+ * calls give identical bits. A shape whose K fits one slice (1024 elements) stores Y from the first
+ * kernel and needs no workspace. Other shapes run exactly as attnq_gemm_nvfp4_small_m.
+ * ws: caller-owned device memory of at least attnq_gemm_nvfp4_small_m_splitk_workspace(N, K, M)
+ * bytes (0: not needed, ws may be NULL), 256-byte aligned, contents irrelevant on entry and
+ * overwritten; calls that share one workspace must be ordered on one stream.
+ * Errors: as attnq_gemm_nvfp4_small_m; ATTNQ_ERR_NULL for a NULL ws that is needed,
+ * ATTNQ_ERR_SHAPE for ws_bytes below the size the shape needs, ATTNQ_ERR_ALIGN for a misaligned ws. */
+ATTNQ_API attnq_status attnq_gemm_nvfp4_small_m_splitk(const attnq_nvfp4* W, const uint16_t* X, int32_t M,
+                                             int32_t ldx, float* Y, int32_t ldy, void* ws, int64_t ws_bytes,
+                                             attnq_stream stream);
+
+/* Bytes of workspace attnq_gemm_nvfp4_small_m_splitk needs for an [N][K] weight and M tokens (0 when
+ * that shape has no slices), or -1 if N < 0, K is not a positive multiple of 32 or M is outside
+ * [0, 16]. Host only, no GPU call. */
+ATTNQ_API int64_t attnq_gemm_nvfp4_small_m_splitk_workspace(int32_t N, int32_t K, int32_t M);
+
 /* Measurement aid, not part of the decode path: read a_bytes at a and then b_bytes at b once, as a
  * plain streaming read (16-byte non-temporal loads, four in flight per lane, 4096 workgroups of 256
  * threads: a grid-stride walk, or one contiguous stretch per workgroup from 1 GiB up) that writes

@@ -49,6 +49,7 @@ _SIGS = {
     "attnq_gemv_bf16": [_P, _I, _I, _P, _P, _P],
     "attnq_gemm_nvfp4_small_m": [ctypes.POINTER(_NVFP4), _P, _I, _I, _P, _I, _P],
     "attnq_read_ceiling": [_P, ctypes.c_int64, _P, ctypes.c_int64, _P, _P],
+    "attnq_gemm_nvfp4_small_m_splitk": [ctypes.POINTER(_NVFP4), _P, _I, _I, _P, _I, _P, ctypes.c_int64, _P],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -57,6 +58,8 @@ _lib.attnq_gemv_nvfp4_lowrank_workspace.argtypes = [_I, _I, _I]
 _lib.attnq_gemv_nvfp4_lowrank_workspace.restype = ctypes.c_int64
 _lib.attnq_gemv_nvfp4_splitk_workspace.argtypes = [_I, _I]
 _lib.attnq_gemv_nvfp4_splitk_workspace.restype = ctypes.c_int64
+_lib.attnq_gemm_nvfp4_small_m_splitk_workspace.argtypes = [_I, _I, _I]
+_lib.attnq_gemm_nvfp4_small_m_splitk_workspace.restype = ctypes.c_int64
 _lib.attnq_status_string.argtypes = [_S]
 _lib.attnq_status_string.restype = ctypes.c_char_p
 
@@ -191,6 +194,24 @@ def attnq_read_ceiling(a, b, sink, stream=None) -> None:
     na = a.numel() * a.element_size()
     nb = 0 if b is None else b.numel() * b.element_size()
     _check(_lib.attnq_read_ceiling(_ptr(a), na, _ptr(b), nb, _ptr(sink, 4), _stream(stream)))
+
+
+def attnq_gemm_nvfp4_small_m_splitk_workspace(N: int, K: int, M: int) -> int:
+    return int(_lib.attnq_gemm_nvfp4_small_m_splitk_workspace(N, K, M))
+
+
+def small_m_workspace(N: int, K: int, M: int, device="cuda") -> torch.Tensor | None:
+    """A workspace for attnq_gemm_nvfp4_small_m_splitk (None if the shape needs none)."""
+    n = attnq_gemm_nvfp4_small_m_splitk_workspace(N, K, M)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def attnq_gemm_nvfp4_small_m_splitk(W: NVFP4Weight, X, Y, ws, stream=None) -> None:
+    M = X.shape[0]
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.attnq_gemm_nvfp4_small_m_splitk(ctypes.byref(W.desc()), _ptr(X, 2), M, X.stride(0) if M else W.K,
+                                                _ptr(Y, 4), Y.stride(0) if M else W.N, _ptr(ws), nbytes,
+                                                _stream(stream)))
 
 
 def raw_library() -> ctypes.CDLL:

@@ -157,6 +157,28 @@ attnq_status attnq_gemm_nvfp4_small_m(const attnq_nvfp4* W, const uint16_t* X, i
   return from_hip(attnq::launch_gemm_nvfp4_small_m(*W, X, M, ldx, Y, ldy, static_cast<hipStream_t>(stream)));
 }
 
+attnq_status attnq_gemm_nvfp4_small_m_splitk(const attnq_nvfp4* W, const uint16_t* X, int32_t M, int32_t ldx, float* Y,
+                                             int32_t ldy, void* ws, int64_t ws_bytes, attnq_stream stream) {
+  attnq_status st = check_nvfp4(W);
+  if (st != ATTNQ_OK) return st;
+  if (M < 0 || M > kMaxM || ldx < W->K || ldx % 8 != 0 || ldy < W->N) return ATTNQ_ERR_SHAPE;
+  if (M > 0 && (int64_t)(M - 1) * ldx + W->K >= (int64_t{1} << 30)) return ATTNQ_ERR_SHAPE;
+  if ((X == nullptr || Y == nullptr) && M != 0 && W->N != 0) return ATTNQ_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(Y, 4)) return ATTNQ_ERR_ALIGN;
+  const int64_t need = attnq::gemm_small_m_splitk_workspace_bytes(W->N, W->K, M);
+  if (need > 0) {
+    if (ws == nullptr) return ATTNQ_ERR_NULL;
+    if (ws_bytes < need) return ATTNQ_ERR_SHAPE;
+    if (!aligned(ws, 256)) return ATTNQ_ERR_ALIGN;
+  }
+  return from_hip(attnq::launch_gemm_nvfp4_small_m_splitk(*W, X, M, ldx, Y, ldy, ws, static_cast<hipStream_t>(stream)));
+}
+
+int64_t attnq_gemm_nvfp4_small_m_splitk_workspace(int32_t N, int32_t K, int32_t M) {
+  if (N < 0 || K <= 0 || K % 32 != 0 || M < 0 || M > kMaxM) return -1;
+  return attnq::gemm_small_m_splitk_workspace_bytes(N, K, M);
+}
+
 attnq_status attnq_read_ceiling(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes, uint32_t* sink,
                                 attnq_stream stream) {
   if (a_bytes < 0 || b_bytes < 0 || a_bytes % 16 != 0 || b_bytes % 16 != 0) return ATTNQ_ERR_SHAPE;

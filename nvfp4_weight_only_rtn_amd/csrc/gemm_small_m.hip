@@ -392,6 +392,170 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_scaled(const ui
   }
 }
 
+// One-shot slices (k_gemm_small_m_slices): the weights are read the way the batch-1 kernels read
+// them, and a wave-private LDS tile turns them into MFMA operands. Workgroup b takes row group b /
+// nslices (WAVES tiles of 16 rows, one per wave) and K slice b % nslices (S steps of 1024 elements).
+// Every load of the slice is issued at once: per step and wave, 8 code loads (each half-wave reads
+// 512 contiguous bytes of one row) and the matching scale loads, and the workgroup's pieces of the
+// slice's X windows (M tokens x 1024 elements each), loaded ahead of the weights and staged in LDS.
+// Per step, a wave moves its codes into its tile as [row][512 B] (pitch 528, so the 16 rows of a
+// read start in different banks) and its scales transposed to [row][lane group][q] (pitch 80);
+// lane (g, i) then reads row i's chunk 4 q + g (16 code bytes, 32 elements) with one 16-byte read,
+// and its eight chunks' scales with another. MFMA (q, d) takes, in lane group g, elements
+// 32 (4 q + g) + 8 d .. + 7: A = X of token i (tokens as rows; rows past M read token M - 1 and are
+// never stored), B = the codes decoded with their E4M3 block scale (exact, decode8_scaled); four
+// accumulator chains (one per d) are added at the end. A slice's raw partial sums go to the
+// workspace, and a second kernel adds the slices in slice order, applies the tensor scale and stores
+// Y; a shape of one slice stores Y directly. (Adding the slices in the same launch, by the last
+// workgroup to take a ticket as in the split-K GEMV, measured slower here: the publication's round
+// trips hold each workgroup's 72 KB of LDS, which is what limits how many run per compute unit.)
+constexpr int kSlStep = 1024;                       // K elements per step
+constexpr int kSlCodePitch = kSlStep / 2 + 16;      // bytes per row of a wave's code tile
+constexpr int kSlScalePitch = 80;                   // bytes per row of a wave's scale tile (64 used)
+constexpr int kSlXPitch = 2 * kSlStep + 16;         // bytes per token row of an X window
+
+template <int MT, int WAVES, int S>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_small_m_slices(const uint8_t* __restrict__ codes,
+                                                                    const uint8_t* __restrict__ scales,
+                                                                    const float* __restrict__ tensor_scale,
+                                                                    SegTable segs, const uint16_t* __restrict__ X,
+                                                                    int M, int ldx, float* __restrict__ Y, int ldy,
+                                                                    int N, int K, int nslices, float* ws) {
+  constexpr int kWinPieces = MT * kSlStep / 8;                             // 16-byte pieces of one X window
+  constexpr int kXPieces = S * kWinPieces;
+  constexpr int kXPerThread = (kXPieces + 64 * WAVES - 1) / (64 * WAVES);
+  constexpr int kRows = 16 * WAVES;
+  __shared__ __align__(16) uint8_t ctile[WAVES][16 * kSlCodePitch];
+  __shared__ __align__(16) uint8_t stile[WAVES][16 * kSlScalePitch];
+  __shared__ __align__(16) uint8_t xwin[S][MT * kSlXPitch];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, i = lane & 15;
+  const int half = lane >> 5, c_lane = lane & 31;              // load layout: half-wave row, chunk
+  const int rg = blockIdx.x / nslices, sl = blockIdx.x - rg * nslices;
+  const int row0 = rg * kRows + 16 * wave;
+  const uint32_t code_pitch = (uint32_t)K >> 1, scale_pitch = (uint32_t)K >> 4;
+  const int cpr = K >> 5;                                       // 32-element chunks per row
+  const int nsteps = (cpr + 31) >> 5;
+  const int st0 = sl * S;
+  const int xi = min(i, M - 1);
+
+  // X windows of the slice first (their latency overlaps the weights'), then every weight load
+  u32x4 xv[kXPerThread];
+#pragma unroll
+  for (int j = 0; j < kXPerThread; ++j) {
+    const int p = min((int)threadIdx.x + j * 64 * WAVES, kXPieces - 1);
+    const int s = p / kWinPieces, r = p - s * kWinPieces;
+    const int m = min(r / (kSlStep / 8), M - 1), e = (st0 + s) * kSlStep + 8 * (r % (kSlStep / 8));
+    xv[j] = *reinterpret_cast<const u32x4*>(X + (size_t)m * ldx + min(e, K - 8));
+  }
+  uint32_t crow[8], srow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t row = (uint32_t)min(row0 + 2 * j + half, N - 1);     // rows past N load row N-1, never stored
+    crow[j] = row * code_pitch;
+    srow[j] = row * scale_pitch;
+  }
+  u32x4 cv[S][8];
+  uint32_t sv[S][8];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = min((st0 + s) * 32 + c_lane, cpr - 1);      // clamped; chunks past the row are zeroed below
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      cv[s][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + (crow[j] + 16u * (uint32_t)c)));
+      sv[s][j] = *reinterpret_cast<const uint16_t*>(scales + (srow[j] + 2u * (uint32_t)c));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kXPerThread; ++j) {
+    const int p = (int)threadIdx.x + j * 64 * WAVES;
+    if (p < kXPieces) {
+      const int s = p / kWinPieces, r = p - s * kWinPieces;
+      const int m = r / (kSlStep / 8), e = (st0 + s) * kSlStep + 8 * (r % (kSlStep / 8));
+      *reinterpret_cast<u32x4*>(&xwin[s][m * kSlXPitch + 16 * (r % (kSlStep / 8))]) =
+          (m < M && e < K) ? xv[j] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) acc[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  uint8_t* ct = ctile[wave];
+  uint8_t* st = stile[wave];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int step = st0 + s;
+    if (step < nsteps) {
+      const int nck = min(32, cpr - step * 32);                 // valid chunks in this step
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = 2 * j + half;
+        *reinterpret_cast<u32x4*>(ct + row * kSlCodePitch + 16 * c_lane) = c_lane < nck ? cv[s][j] : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint16_t*>(st + row * kSlScalePitch + 16 * (c_lane & 3) + 2 * (c_lane >> 2)) = (uint16_t)sv[s][j];
+      }
+      const u32x4 sc = *reinterpret_cast<const u32x4*>(st + i * kSlScalePitch + 16 * g);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (4 * q < nck) {
+          const u32x4 cw = *reinterpret_cast<const u32x4*>(ct + i * kSlCodePitch + 16 * (4 * q + g));
+          const uint8_t* xp = &xwin[s][xi * kSlXPitch + 64 * (4 * q + g)];
+          const uint32_t sb = word(sc, q >> 1) >> (16 * (q & 1));        // the chunk's two block scales
+          const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0), s1 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 1);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const u32x4 xa = *reinterpret_cast<const u32x4*>(xp + 16 * d);
+            acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), decode8_scaled(word(cw, d), d < 2 ? s0 : s1),
+                                                             acc[d], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  const f32x4 a4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+  // lane (g, i): tokens 4 g + v of weight row row0 + i
+  const int row = row0 + i;
+  if (nslices == 1) {
+    if (row < N) {
+      const float ts = tensor_scale[segment_of(segs, row)];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (4 * g + v < M) Y[(size_t)(4 * g + v) * ldy + row] = a[v] * ts;
+    }
+    return;
+  }
+  // the slice's raw partial sums: part[row group][slice][token][row of the group]
+  float* part = reinterpret_cast<float*>(ws) + (size_t)rg * nslices * M * kRows + 16 * wave + i;
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    if (4 * g + v < M) part[((size_t)sl * M + 4 * g + v) * kRows] = a[v];
+}
+
+// Second kernel of a sliced product (stream order makes the partials visible): thread (m, row) adds
+// the row group's slices in slice order, applies the tensor scale and stores Y[m][row].
+__global__ __launch_bounds__(256) void k_gemm_small_m_slices_sum(const float* __restrict__ part,
+                                                                 const float* __restrict__ tensor_scale, SegTable segs,
+                                                                 float* __restrict__ Y, int ldy, int M, int N,
+                                                                 int nslices) {
+  const int row = blockIdx.x * 256 + threadIdx.x, m = blockIdx.y;
+  if (row >= N) return;
+  const int rg = row >> 6, r = row & 63;
+  const float* p = part + ((size_t)rg * nslices * M + m) * 64 + r;
+  float t = 0.0f;
+  int k = 0;
+  for (; k + 4 <= nslices; k += 4) {                     // four loads in flight, added in order
+    const float a0 = p[(size_t)k * M * 64], a1 = p[(size_t)(k + 1) * M * 64];
+    const float a2 = p[(size_t)(k + 2) * M * 64], a3 = p[(size_t)(k + 3) * M * 64];
+    t += a0;
+    t += a1;
+    t += a2;
+    t += a3;
+  }
+  for (; k < nslices; ++k) t += p[(size_t)k * M * 64];
+  Y[(size_t)m * ldy + row] = t * tensor_scale[segment_of(segs, row)];
+}
+
 template <int RT>
 void launch_scaled(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy, int ks,
                    hipStream_t stream) {
@@ -418,12 +582,69 @@ void launch_mfma(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float*
                                                            W.N, W.K, per);
 }
 
+// Launch plan of the one-shot slices: rows of more than 6144 elements, and weights of at least 16384
+// rows at M > 4; 4 waves (64 rows) per workgroup and slices of one step (two for 4 < M <= 8 on
+// weights of at least 16384 rows). Measured per launch over 8 distinct 31B-like layers in graph
+// replays, slices and their sum kernel against the older kernels: at M = 8 down 26.5 against
+// 39.9 us, gate|up 45.7 against 58.2, but q|k|v 14.3 against 12.8 and o 11.0 against 10.1 (which
+// keep the older kernels); at M = 16 down 27.8 against 47.6 and gate|up 51.9 against 68.2; at M = 4
+// down 23.0 against 29.6 (the other projections stay on the batch-1 walk). Workgroups of 2 or 8
+// waves and slices of 3 steps measured slower in a timing copy.
+struct SlicePlan {
+  int mt, s, nslices, groups;
+};
+
+bool slice_plan(const attnq_nvfp4& W, int M, SlicePlan* p) {
+  if (M < 1 || M > 16 || (W.K <= 6144 && (M <= 4 || W.N < 16384))) return false;
+  p->mt = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
+  p->s = (p->mt == 8 && W.N >= 16384) ? 2 : 1;
+  const int nsteps = (W.K / 32 + 31) / 32;
+  p->nslices = (nsteps + p->s - 1) / p->s;
+  p->groups = (W.N + 63) / 64;
+  return true;
+}
+
+template <int MT, int S>
+void launch_slices_t(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy, const SlicePlan& p,
+                     float* ws, hipStream_t stream) {
+  SegTable t;
+  t.n_seg = W.n_seg;
+  for (int s = 0; s < ATTNQ_MAX_SEGMENTS; ++s) t.end[s] = (s < W.n_seg) ? W.seg_end[s] : W.N;
+  k_gemm_small_m_slices<MT, 4, S><<<(unsigned)(p.groups * p.nslices), 256, 0, stream>>>(
+      W.codes, W.scales, W.tensor_scale, t, X, M, ldx, Y, ldy, W.N, W.K, p.nslices, ws);
+  if (p.nslices > 1)
+    k_gemm_small_m_slices_sum<<<dim3((unsigned)((W.N + 255) / 256), (unsigned)M), 256, 0, stream>>>(
+        ws, W.tensor_scale, t, Y, ldy, M, W.N, p.nslices);
+}
+
 // K split: 12 waves per workgroup (at most one per superchunk). Timed on MI355X over the
 // 31B-like layer shapes at M = 4, 8, 16 and row tiles of 1, 2, 4: two 16-row tiles per wave and
 // 12 waves are within 5% of the best configuration for every shape.
 int pick_ks(const attnq_nvfp4& W) { return max(1, min(12, W.K / kSuper)); }
 
 }  // namespace
+
+int64_t gemm_small_m_splitk_workspace_bytes(int N, int K, int M) {
+  attnq_nvfp4 W{};
+  W.N = N;
+  W.K = K;
+  SlicePlan p;
+  if (N == 0 || !slice_plan(W, M, &p) || p.nslices == 1) return 0;
+  return (int64_t)p.groups * p.nslices * M * 64 * 4;
+}
+
+hipError_t launch_gemm_nvfp4_small_m_splitk(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
+                                            void* ws, hipStream_t stream) {
+  if (W.N == 0 || M == 0) return hipSuccess;
+  SlicePlan p;
+  if (!slice_plan(W, M, &p)) return launch_gemm_nvfp4_small_m(W, X, M, ldx, Y, ldy, stream);
+  float* w = static_cast<float*>(ws);
+  if (p.mt == 4) launch_slices_t<4, 1>(W, X, M, ldx, Y, ldy, p, w, stream);
+  else if (p.mt == 8 && p.s == 2) launch_slices_t<8, 2>(W, X, M, ldx, Y, ldy, p, w, stream);
+  else if (p.mt == 8) launch_slices_t<8, 1>(W, X, M, ldx, Y, ldy, p, w, stream);
+  else launch_slices_t<16, 1>(W, X, M, ldx, Y, ldy, p, w, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_nvfp4_small_m(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
                                      hipStream_t stream) {

@@ -29,6 +29,11 @@ hipError_t launch_read_ceiling(const void* a, int64_t a_bytes, const void* b, in
 hipError_t launch_gemv_bf16(const uint16_t* W, int N, int K, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_gemm_nvfp4_small_m(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
                                      hipStream_t stream);
+// the same with K cut into one-shot slices on separate workgroups (workspace: fixed ticket area, then
+// the slices' partial sums); shapes without slices run launch_gemm_nvfp4_small_m
+hipError_t launch_gemm_nvfp4_small_m_splitk(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
+                                            void* ws, hipStream_t stream);
+int64_t gemm_small_m_splitk_workspace_bytes(int N, int K, int M);
 // M = 1 .. 4 on the batch-1 walk for rows of at most 192 chunks; false (nothing launched) otherwise
 bool launch_gemm_nvfp4_tokens(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
                               hipStream_t stream);

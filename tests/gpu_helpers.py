@@ -8,7 +8,8 @@ Comparison rules:
   float64 oracle; the tests also hold every element to
   |y - y_ref| <= 2^-16 * sum_k |x_k w_k|, a bound far above fp32 summation error for any
   order (about K/64 + 20 roundings of 2^-24) yet below the contribution of a single dropped or
-  mis-scaled 16-element block.
+  mis-scaled 16-element block, and the vector to an internal relative L2 of 1e-5, taken against
+  the larger of |y_ref| and 2^-10 |sum_k |x_k w_k|| (the scale of the rounding error).
 """
 import sys
 
@@ -19,6 +20,7 @@ import oracle as O
 
 REL_L2_CONTRACT = 1e-3
 REL_L2_INTERNAL = 1e-5
+INTERNAL_FLOOR = 2.0 ** -10
 ELEM_BOUND = 2.0 ** -16
 
 
@@ -92,4 +94,9 @@ def assert_close_products(y: np.ndarray, y_ref: np.ndarray, absdot: np.ndarray, 
     nref = np.linalg.norm(y_ref)
     rel = np.linalg.norm(y - y_ref) / nref if nref > 0 else np.linalg.norm(y - y_ref)
     assert rel <= REL_L2_CONTRACT, f"{what}: rel-L2 {rel} over the 1e-3 contract"
-    assert rel <= REL_L2_INTERNAL, f"{what}: rel-L2 {rel} over the 1e-5 internal gate"
+    # The internal gate is relative to the larger of |y_ref| and 2^-10 |sum_k |x_k w_k||: the rounding
+    # error of any fp32 summation order scales with the latter, so a vector whose entries cancel
+    # to 10^4 times below it (a single output row, say) is held to the arithmetic, not to its norm.
+    floor = INTERNAL_FLOOR * np.linalg.norm(np.asarray(absdot, dtype=np.float64))
+    rel_int = np.linalg.norm(y - y_ref) / max(nref, floor) if max(nref, floor) > 0 else np.linalg.norm(y - y_ref)
+    assert rel_int <= REL_L2_INTERNAL, f"{what}: rel-L2 {rel_int} over the 1e-5 internal gate"

@@ -31,7 +31,7 @@ def test_header_declares_every_call():
               "attnq_gemm_nvfp4_small_m", "attnq_gemv_nvfp4_glu", "attnq_gemv_nvfp4_lowrank",
               "attnq_gemv_nvfp4_lowrank_workspace", "attnq_gemv_nvfp4_splitk",
               "attnq_gemv_nvfp4_splitk_workspace", "attnq_gemv_nvfp4_splitk_noalloc", "attnq_read_ceiling",
-              "attnq_status_string"]:
+              "attnq_gemm_nvfp4_small_m_splitk", "attnq_gemm_nvfp4_small_m_splitk_workspace", "attnq_status_string"]:
         assert n in names
 
 
@@ -69,6 +69,24 @@ def test_splitk_workspace_sizes():
     assert ws(100, 49152 + 32) == 0                    # would need 13 slices: not split
     assert ws(0, 21504) == 0
     for bad in [(-1, 21504), (64, 0), (64, 48)]:
+        assert ws(*bad) == -1
+
+
+def test_small_m_splitk_workspace_sizes():
+    ws = A.attnq_gemm_nvfp4_small_m_splitk_workspace
+    # fp32 partials [row group of 64][slice][token][64 rows]
+    # gate|up 43008 x 5376 at M = 8: 672 groups, 6 steps of 1024 in slices of 2 -> 3
+    assert ws(43008, 5376, 8) == 672 * 3 * 8 * 64 * 4
+    # down 5376 x 21504 at M = 4: 84 groups, 21 one-step slices
+    assert ws(5376, 21504, 4) == 84 * 21 * 4 * 64 * 4
+    # 16384 x 4096 at M = 16: 256 groups, 4 one-step slices
+    assert ws(16384, 4096, 16) == 256 * 4 * 16 * 64 * 4
+    assert ws(5376, 4096, 16) == 0                     # fewer rows and short rows: the older kernels
+    assert ws(6144, 5376, 4) == 0                      # M <= 4 on rows of up to 6144: the batch-1 walk
+    assert ws(16384, 1024, 8) == 0                     # one slice: Y stored directly
+    assert ws(300000, 4096, 8) == 4688 * 2 * 8 * 64 * 4   # 4 steps in slices of 2
+    assert ws(0, 4096, 8) == 0 and ws(64, 4096, 0) == 0
+    for bad in [(-1, 4096, 8), (64, 48, 8), (64, 4096, 17), (64, 4096, -1)]:
         assert ws(*bad) == -1
 
 
@@ -206,6 +224,15 @@ def test_gemv_and_gemm_validation():
     assert na(ctypes.byref(down), None, FAKE, None) == 1
     assert na(ctypes.byref(down), FAKE + 8, FAKE, None) == 3
     assert na(ctypes.byref(_nv(layout=1)), FAKE, FAKE, None) == 5
+    smk = lib.attnq_gemm_nvfp4_small_m_splitk
+    gu = _nv(N=43008, K=5376, n_seg=2, seg_end=[21504, 43008])
+    need = A.attnq_gemm_nvfp4_small_m_splitk_workspace(43008, 5376, 8)
+    assert smk(ctypes.byref(gu), FAKE, 8, 5376, FAKE, 43008, None, need, None) == 1        # workspace needed
+    assert smk(ctypes.byref(gu), FAKE, 8, 5376, FAKE, 43008, FAKE, need - 1, None) == 2    # too small
+    assert smk(ctypes.byref(gu), FAKE, 8, 5376, FAKE, 43008, FAKE + 64, need, None) == 3   # 256-byte alignment
+    assert smk(ctypes.byref(gu), FAKE, 17, 5376, FAKE, 43008, FAKE, need, None) == 2       # M > 16
+    assert smk(ctypes.byref(gu), FAKE, 8, 5370, FAKE, 43008, FAKE, need, None) == 2        # ldx % 8
+    assert smk(ctypes.byref(gu), None, 8, 5376, FAKE, 43008, FAKE, need, None) == 1
     rc = lib.attnq_read_ceiling
     assert rc(FAKE, 24, None, 0, FAKE, None) == 2                                 # not a multiple of 16
     assert rc(FAKE, -16, None, 0, FAKE, None) == 2

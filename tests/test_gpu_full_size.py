@@ -75,6 +75,14 @@ def _check_projection(A, name, bundles, seg_rows, K, x, X=None):
         assert np.isfinite(Yh).all()
         assert_close_products(Yh[:, rows], O.gemm_nvfp4_small_m(c, s, t, X, sseg), O.abs_dot(c, s, t, X, sseg),
                               f"{name} small-M {M}")
+        say(f"full-size {name} small-M {M}, K slices")
+        Y.fill_(float("nan"))
+        A.attnq_gemm_nvfp4_small_m_splitk(W, dev(X), Y, A.small_m_workspace(W.N, K, M))
+        torch.cuda.synchronize()
+        Yh = host(Y)
+        assert np.isfinite(Yh).all()
+        assert_close_products(Yh[:, rows], O.gemm_nvfp4_small_m(c, s, t, X, sseg), O.abs_dot(c, s, t, X, sseg),
+                              f"{name} small-M {M}, K slices")
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
@@ -97,6 +105,11 @@ def test_31b_layer_projection(A, name):
         torch.cuda.synchronize()
         assert_close_products(host(Y)[:, rows], O.gemm_nvfp4_small_m(c, s, t, X[:4], sseg),
                               O.abs_dot(c, s, t, X[:4], sseg), f"{name} small-M 4")
+        Y.fill_(float("nan"))
+        A.attnq_gemm_nvfp4_small_m_splitk(W, dev(X[:4]), Y, A.small_m_workspace(W.N, K, 4))
+        torch.cuda.synchronize()
+        assert_close_products(host(Y)[:, rows], O.gemm_nvfp4_small_m(c, s, t, X[:4], sseg),
+                              O.abs_dot(c, s, t, X[:4], sseg), f"{name} small-M 4, K slices")
 
 
 def test_lm_head_bf16_full_size(A):
