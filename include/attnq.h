@@ -124,6 +124,24 @@ ATTNQ_API attnq_status attnq_reconstruct(const attnq_theta* theta, uint16_t* W_e
 ATTNQ_API attnq_status attnq_quantize_nvfp4(const attnq_theta* theta, const attnq_nvfp4* dst, int32_t seg,
                                   attnq_stream stream);
 
+/* The same result as attnq_quantize_nvfp4, bit for bit, with W_eff rebuilt once instead of twice
+ * ("Throughput", "What quantization actually saves": the rebuild is load-time work). The first
+ * kernel rebuilds W_eff, folds its amax into the tensor scale and writes it as bf16 into the
+ * workspace; the second rounds it to NVFP4 from there. At r == 0 there is nothing to rebuild and
+ * the call is attnq_quantize_nvfp4 (the workspace is not touched and may be NULL).
+ * workspace: caller-owned device memory of at least attnq_quantize_nvfp4_staged_workspace(N, K, r)
+ * bytes (2 N K for r > 0), 256-byte aligned, overlapping neither theta's arrays nor dst; its
+ * contents on entry do not matter and it holds W_eff on return. Calls that share a workspace must
+ * be ordered (one stream).
+ * Errors: as attnq_quantize_nvfp4, plus ATTNQ_ERR_NULL for a NULL workspace, ATTNQ_ERR_SHAPE for
+ * workspace_bytes below the size, ATTNQ_ERR_ALIGN for a misaligned workspace (r > 0 only). */
+ATTNQ_API attnq_status attnq_quantize_nvfp4_staged(const attnq_theta* theta, const attnq_nvfp4* dst, int32_t seg,
+                                                   void* workspace, int64_t workspace_bytes, attnq_stream stream);
+
+/* Workspace bytes for attnq_quantize_nvfp4_staged on an [N][K] projection of rank r: 2 N K for
+ * r > 0 and N, K > 0, else 0. */
+ATTNQ_API int64_t attnq_quantize_nvfp4_staged_workspace(int32_t N, int32_t K, int32_t r);
+
 /* y[n] = sum_k x[k] * weight[n][k] for an NVFP4 weight: one kernel that reads codes and
  * scales once and decodes fp4 in registers ("Where GPU time goes": no dequant pass).
  * x [K] bf16 16-byte aligned; y [N] fp32 4-byte aligned, must not overlap x or the weight.

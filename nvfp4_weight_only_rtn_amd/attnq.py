@@ -41,6 +41,7 @@ _I = ctypes.c_int32
 _SIGS = {
     "attnq_reconstruct": [ctypes.POINTER(_Theta), _P, _P],
     "attnq_quantize_nvfp4": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), _I, _P],
+    "attnq_quantize_nvfp4_staged": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), _I, _P, ctypes.c_int64, _P],
     "attnq_gemv_nvfp4": [ctypes.POINTER(_NVFP4), _P, _P, _P],
     "attnq_gemv_nvfp4_splitk": [ctypes.POINTER(_NVFP4), _P, _P, _P, ctypes.c_int64, _P],
     "attnq_gemv_nvfp4_splitk_noalloc": [ctypes.POINTER(_NVFP4), _P, _P, _P],
@@ -56,6 +57,8 @@ for _name, _args in _SIGS.items():
     getattr(_lib, _name).restype = _S
 _lib.attnq_gemv_nvfp4_lowrank_workspace.argtypes = [_I, _I, _I]
 _lib.attnq_gemv_nvfp4_lowrank_workspace.restype = ctypes.c_int64
+_lib.attnq_quantize_nvfp4_staged_workspace.argtypes = [_I, _I, _I]
+_lib.attnq_quantize_nvfp4_staged_workspace.restype = ctypes.c_int64
 _lib.attnq_gemv_nvfp4_splitk_workspace.argtypes = [_I, _I]
 _lib.attnq_gemv_nvfp4_splitk_workspace.restype = ctypes.c_int64
 _lib.attnq_gemm_nvfp4_small_m_splitk_workspace.argtypes = [_I, _I, _I]
@@ -135,6 +138,24 @@ def attnq_reconstruct(W0, s, U, V, W_eff, stream=None) -> None:
 def attnq_quantize_nvfp4(W0, s, U, V, dst: NVFP4Weight, seg: int = 0, stream=None) -> None:
     th = _theta(W0, s, U, V)
     _check(_lib.attnq_quantize_nvfp4(ctypes.byref(th), ctypes.byref(dst.desc()), seg, _stream(stream)))
+
+
+def attnq_quantize_nvfp4_staged_workspace(N: int, K: int, r: int) -> int:
+    return int(_lib.attnq_quantize_nvfp4_staged_workspace(N, K, r))
+
+
+def staged_workspace(N: int, K: int, r: int, device="cuda") -> torch.Tensor | None:
+    """A workspace for attnq_quantize_nvfp4_staged on an [N][K] projection of rank r (None if not
+    needed); torch's allocations are 256-byte aligned."""
+    n = attnq_quantize_nvfp4_staged_workspace(N, K, r)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def attnq_quantize_nvfp4_staged(W0, s, U, V, dst: NVFP4Weight, ws, seg: int = 0, stream=None) -> None:
+    th = _theta(W0, s, U, V)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.attnq_quantize_nvfp4_staged(ctypes.byref(th), ctypes.byref(dst.desc()), seg, _ptr(ws), nbytes,
+                                            _stream(stream)))
 
 
 def attnq_gemv_nvfp4(W: NVFP4Weight, x, y, stream=None) -> None:

@@ -35,9 +35,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source additions. quantize.hip: matrix-core results in ordinary VGPRs, so that the rebuild's
+# epilogue reads its accumulators without AGPR-to-VGPR copies.
+EXTRA_FLAGS = {"quantize.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

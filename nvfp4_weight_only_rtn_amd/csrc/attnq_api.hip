@@ -72,6 +72,32 @@ attnq_status attnq_quantize_nvfp4(const attnq_theta* theta, const attnq_nvfp4* d
   return from_hip(attnq::launch_quantize(*theta, codes, scales, dst->tensor_scale + seg, static_cast<hipStream_t>(stream)));
 }
 
+attnq_status attnq_quantize_nvfp4_staged(const attnq_theta* theta, const attnq_nvfp4* dst, int32_t seg, void* workspace,
+                                         int64_t workspace_bytes, attnq_stream stream) {
+  attnq_status st = check_theta(theta);
+  if (st != ATTNQ_OK) return st;
+  st = check_nvfp4(dst);
+  if (st != ATTNQ_OK) return st;
+  if (theta->K != dst->K) return ATTNQ_ERR_SHAPE;
+  if (seg < 0 || seg >= dst->n_seg) return ATTNQ_ERR_SEGMENT;
+  const int32_t start = seg == 0 ? 0 : dst->seg_end[seg - 1];
+  if (dst->seg_end[seg] - start != theta->N) return ATTNQ_ERR_SEGMENT;
+  const int64_t need = attnq::quantize_staged_workspace_bytes(theta->N, theta->K, theta->r);
+  if (need > 0) {
+    if (workspace == nullptr) return ATTNQ_ERR_NULL;
+    if (workspace_bytes < need) return ATTNQ_ERR_SHAPE;
+    if (!aligned(workspace, 256)) return ATTNQ_ERR_ALIGN;
+  }
+  uint8_t* codes = dst->codes + (size_t)start * (dst->K / 2);
+  uint8_t* scales = dst->scales + (size_t)start * (dst->K / 16);
+  return from_hip(attnq::launch_quantize_staged(*theta, codes, scales, dst->tensor_scale + seg, workspace,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int64_t attnq_quantize_nvfp4_staged_workspace(int32_t N, int32_t K, int32_t r) {
+  return attnq::quantize_staged_workspace_bytes(N, K, r);
+}
+
 attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y, attnq_stream stream) {
   attnq_status st = check_nvfp4(W);
   if (st != ATTNQ_OK) return st;

@@ -11,6 +11,10 @@ namespace attnq {
 hipError_t launch_reconstruct(const attnq_theta& theta, uint16_t* W_eff, hipStream_t stream);
 hipError_t launch_quantize(const attnq_theta& theta, uint8_t* codes, uint8_t* scales, float* tensor_scale,
                            hipStream_t stream);
+// the same with W_eff rebuilt once into `workspace` (bf16 [N][K]) and quantized from there
+hipError_t launch_quantize_staged(const attnq_theta& theta, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                  void* workspace, hipStream_t stream);
+int64_t quantize_staged_workspace_bytes(int32_t N, int32_t K, int32_t r);
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream);
 // K split across workgroups for rows of 16384 elements or more (other shapes: launch_gemv_nvfp4);
 // ws holds the tickets (zero on entry, zero again on exit) and the partial sums

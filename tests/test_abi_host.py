@@ -27,7 +27,8 @@ def _declared_functions():
 
 def test_header_declares_every_call():
     names = _declared_functions()
-    for n in ["attnq_reconstruct", "attnq_quantize_nvfp4", "attnq_gemv_nvfp4", "attnq_gemv_bf16",
+    for n in ["attnq_reconstruct", "attnq_quantize_nvfp4", "attnq_quantize_nvfp4_staged",
+              "attnq_quantize_nvfp4_staged_workspace", "attnq_gemv_nvfp4", "attnq_gemv_bf16",
               "attnq_gemm_nvfp4_small_m", "attnq_gemv_nvfp4_glu", "attnq_gemv_nvfp4_lowrank",
               "attnq_gemv_nvfp4_lowrank_workspace", "attnq_gemv_nvfp4_splitk",
               "attnq_gemv_nvfp4_splitk_workspace", "attnq_gemv_nvfp4_splitk_noalloc", "attnq_read_ceiling",
@@ -166,6 +167,29 @@ def test_quantize_validation():
     assert q(ctypes.byref(_th()), ctypes.byref(_nv(n_seg=5)), 0, None) == 4
     assert q(ctypes.byref(_th()), ctypes.byref(_nv(codes=FAKE + 4)), 0, None) == 3
     assert q(ctypes.byref(_th()), ctypes.byref(_nv(scales=FAKE + 2)), 0, None) == 3
+
+
+def test_quantize_staged_workspace_sizes():
+    ws = A.attnq_quantize_nvfp4_staged_workspace
+    assert ws(5376, 21504, 16) == 2 * 5376 * 21504           # bf16 W_eff of the whole projection
+    assert ws(21504, 5376, 1) == 2 * 21504 * 5376
+    assert ws(64, 64, 0) == 0                                # rank 0: nothing to rebuild
+    assert ws(0, 64, 16) == 0 and ws(64, 0, 16) == 0
+
+
+@no_gpu
+def test_quantize_staged_validation():
+    lib = A.raw_library()
+    q = lib.attnq_quantize_nvfp4_staged
+    need = A.attnq_quantize_nvfp4_staged_workspace(64, 64, 4)
+    r4 = _th(r=4, U=FAKE, V=FAKE)
+    assert q(ctypes.byref(r4), ctypes.byref(_nv()), 0, None, need, None) == 1     # r > 0 needs a workspace
+    assert q(ctypes.byref(r4), ctypes.byref(_nv()), 0, FAKE, need - 1, None) == 2  # too small
+    assert q(ctypes.byref(r4), ctypes.byref(_nv()), 0, FAKE + 16, need, None) == 3  # not 256-byte aligned
+    assert q(ctypes.byref(_th(K=96, r=4, U=FAKE, V=FAKE)), ctypes.byref(_nv()), 0, FAKE, 1 << 20, None) == 2
+    assert q(ctypes.byref(r4), ctypes.byref(_nv()), 1, FAKE, need, None) == 4      # seg out of range
+    assert q(ctypes.byref(_th(r=4)), ctypes.byref(_nv()), 0, FAKE, need, None) == 1  # U, V missing
+    assert q(None, ctypes.byref(_nv()), 0, FAKE, need, None) == 1
 
 
 @no_gpu
