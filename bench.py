@@ -9,8 +9,9 @@ in HBM when timing starts.
 The weights are built on the GPU by the load path itself: seeded bf16 W0 drawn on the device,
 then attnq_quantize_nvfp4 (passthrough reconstruction). The load path is also timed on its
 own workload -- all 410 theta bundles at rank 16 with s ~ U(0.9, 1.1) (420 segment
-quantizations: in 10 layers k's bundle also fills the v rows) -- and so is the small-M verify
-product (M = 4 and 8) on one layer; both are reported as extra fields.
+quantizations: in 10 layers k's bundle also fills the v rows), through the staged call
+(attnq_quantize_nvfp4_staged, one shared workspace) and the two-rebuild call -- and so is the
+small-M verify product (M = 4 and 8) on one layer; both are reported as extra fields.
 
 Three more token streams are timed the same way and reported under "streams": the chained token
 in which each layer's gate|up launch applies the activation epilogue (attnq_gemv_nvfp4_glu)
@@ -294,7 +295,11 @@ def dominant_kernel_timing(model: Model, reps: int):
 
 
 def load_path_timing(A, dev, model: Model, reps: int = 1):
-    """Rank-16 reconstruct + RTN quantize over all 410 theta bundles (420 segment writes)."""
+    """Rank-16 reconstruct + RTN quantize over all 410 theta bundles (420 segment writes), timed
+    twice: the staged call (attnq_quantize_nvfp4_staged: W_eff rebuilt once into one shared
+    workspace, then quantized from it) and the two-rebuild call (attnq_quantize_nvfp4: the rebuild
+    is formed again in the quantize pass). Returns {"staged": ms, "two_rebuilds": ms}, elements,
+    distinct bundles."""
     from nvfp4_weight_only_rtn_amd import inputs
     r = 16
     bundles = []      # (W, seg, W0, s, U, V)
@@ -321,14 +326,22 @@ def load_path_timing(A, dev, model: Model, reps: int = 1):
                 elements += n * K
     torch.cuda.synchronize()
 
-    def run():
+    ws = A.staged_workspace(max(b[2].shape[0] * b[2].shape[1] for b in bundles), 1, r)
+
+    def run_staged():
+        for (W, i, W0, s, U, V) in bundles:
+            A.attnq_quantize_nvfp4_staged(W0, s, U, V, W, ws, seg=i)
+
+    def run_two():
         for (W, i, W0, s, U, V) in bundles:
             A.attnq_quantize_nvfp4(W0, s, U, V, W, seg=i)
-    run()                                   # warm-up (first-touch of every buffer)
-    ms = time_steps(run, reps)
-    del bundles
+    out = {}
+    for name, run in (("staged", run_staged), ("two_rebuilds", run_two)):
+        run()                               # warm-up (first-touch of every buffer)
+        out[name] = time_steps(run, reps)
+    del bundles, ws
     torch.cuda.empty_cache()
-    return ms, elements, distinct
+    return out, elements, distinct
 
 
 def small_m_timing(A, model: Model, steps: int):
@@ -665,12 +678,16 @@ def main():
     if not args.no_load_path:
         log("timing the rank-16 load path over 410 bundles")
         ms, elements, distinct = load_path_timing(A, dev, model)
-        # 4.5625 B per element: W0 read twice (amax pass, quantize pass) + 0.5625 B written
-        nbytes = int(elements * 4.5625)
-        flops = elements * 2 * 16 * 2
-        load = {"ms": round(ms, 3), "elements": elements, "bundles": distinct, "segments": 420,
-                "TBps_algorithmic": round(nbytes / (ms * 1e-3) / 1e12, 3),
-                "fma_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2)}
+        # algorithmic bytes per element -- staged: W0 read, W_eff written and read back (2 + 2 + 2),
+        # 0.5625 B of codes and scales written; two rebuilds: W0 read twice + 0.5625 B written.
+        # Rank-term flops: 2 * 16 per element per rebuild.
+        per = {"staged": (6.5625, 1), "two_rebuilds": (4.5625, 2)}
+        load = {"ms": round(ms["staged"], 3), "call": "attnq_quantize_nvfp4_staged", "elements": elements,
+                "bundles": distinct, "segments": 420}
+        for name, t in ms.items():
+            bpe, rebuilds = per[name]
+            load[name] = {"ms": round(t, 3), "TBps_algorithmic": round(elements * bpe / (t * 1e-3) / 1e12, 3),
+                          "rank_TFLOPs": round(elements * 32 * rebuilds / (t * 1e-3) / 1e12, 2)}
         log(f"load path: {load}")
         model.quantize_passthrough(dev)   # restore the passthrough weights for the stream
 
