@@ -35,9 +35,10 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-source additions. quantize.hip: matrix-core results in ordinary VGPRs, so that the rebuild's
-# epilogue reads its accumulators without AGPR-to-VGPR copies.
-EXTRA_FLAGS = {"quantize.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source additions: matrix-core results in ordinary VGPRs, so that the epilogues (the rebuild's,
+# the small-M products') read their accumulators without AGPR-to-VGPR copies.
+EXTRA_FLAGS = {"quantize.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "gemm_small_m.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

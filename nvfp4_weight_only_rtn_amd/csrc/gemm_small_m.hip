@@ -36,6 +36,8 @@
 // stored. The M <= 4 kernel also loads each superchunk's X together with its weights, one
 // superchunk ahead: load counters complete in order, so X loaded inside the compute step (after
 // the next superchunk's weight loads) would make every wait for X a wait for those weights too.
+#include <atomic>
+
 #include "attnq_device.h"
 #include "launch.h"
 
@@ -273,6 +275,140 @@ __device__ __forceinline__ bf16x8 decode8_scaled(uint32_t w, float s) {
     if (j == 0) r.x = u; else if (j == 1) r.y = u; else if (j == 2) r.z = u; else r.w = u;
   }
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// fp16 operands for the staged-X kernels (slices and walking strips). Decoding to bf16 costs two
+// VALU instructions per weight (a convert to fp32 pairs, a multiply per value and a pack); in fp16
+// it is one convert per pair at scale 1 and one packed multiply by the block scale, which is exact
+// for the same reason (the product's 6 significant bits and its range [2^-10, 2688] fit fp16's
+// normal range). X then has to be fp16 too, and a bf16 value is exactly an fp16 one once scaled by
+// a power of two into fp16's normal range: this holds for a token's values in one staged window when
+// all are finite and every nonzero one lies within 2^29 of the window's largest. The workgroup
+// checks that while staging; if it holds for every token it stores each token's window scaled by
+// 2^(15 - e_max) as fp16, and multiplies that token's sums by the inverse power of two, which is
+// exact: every product and partial sum is the bf16 computation's times a power of two, and the
+// exponent limits below keep every value normal in fp32. Otherwise the window stays bf16.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kF16Span = 29;             // octaves between a window's largest value and its smallest nonzero
+constexpr int kF16MinExp = 127 - 75;     // the largest value's biased exponent: 2^-75 .. 2^105
+constexpr int kF16MaxExp = 127 + 105;
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// 8 E2M1 codes times their E4M3 block scale (both fp16 halves of s2) -> 8 fp16, exact.
+__device__ __forceinline__ f16x8 decode8_f16(uint32_t w, f16x2 s2) {
+  const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2)};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// E4M3 byte h of a dword, in both halves of an fp16 pair (exact: E4M3 values are fp16 normals).
+__device__ __forceinline__ f16x2 e4m3_pair(uint32_t w, int h) {
+  const _Float16 v = (_Float16)(h == 0 ? __builtin_amdgcn_cvt_f32_fp8((int)w, 0) : __builtin_amdgcn_cvt_f32_fp8((int)w, 1));
+  return f16x2{v, v};
+}
+
+// Largest biased exponent of 8 bf16 values; bad is set for inf, NaN and bf16 subnormals.
+__device__ __forceinline__ int piece_emax(const u32x4& v, int& bad) {
+  int e = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t h = (word(v, j >> 1) >> (16 * (j & 1))) & 0x7FFFu;
+    const int f = (int)(h >> 7);
+    e = max(e, f);
+    bad |= (f == 255) | ((f == 0) & (h != 0));
+  }
+  return e;
+}
+
+// Whether every nonzero value of the piece lies within kF16Span octaves of the token's largest.
+__device__ __forceinline__ int piece_out_of_span(const u32x4& v, int emax) {
+  int bad = emax != 0 && (emax < kF16MinExp || emax > kF16MaxExp);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t h = (word(v, j >> 1) >> (16 * (j & 1))) & 0x7FFFu;
+    bad |= (h != 0) & ((int)(h >> 7) < emax - kF16Span);
+  }
+  return bad;
+}
+
+__device__ __forceinline__ float pow2_biased(int e) { return __builtin_bit_cast(float, (uint32_t)e << 23); }
+
+// 8 bf16 values times 2^(15 - (emax - 127)) -> 8 fp16 (exact under piece_out_of_span's conditions).
+__device__ __forceinline__ u32x4 piece_to_f16(const u32x4& v, int emax) {
+  const float sc = emax == 0 ? 1.0f : pow2_biased(127 + 142 - emax);
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = word(v, j);
+    const auto h = __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, w << 16) * sc,
+                                              __builtin_bit_cast(float, w & 0xFFFF0000u) * sc);
+    const uint32_t u = __builtin_bit_cast(uint32_t, h);
+    if (j == 0) r.x = u; else if (j == 1) r.y = u; else if (j == 2) r.z = u; else r.w = u;
+  }
+  return r;
+}
+
+// The inverse of piece_to_f16's factor, applied to a token's sums.
+__device__ __forceinline__ float f16_unscale(int emax) { return emax == 0 ? 1.0f : pow2_biased(emax - 15); }
+
+// A workgroup's X pieces before they go to LDS: tok[j] is piece j's token, or -1 for a piece that
+// is stored as zero. e[16] (LDS) receives each token's largest biased exponent. Returns, the same
+// for every thread, whether the window takes the fp16 operands; the pieces are then converted.
+template <int NP>
+__device__ __forceinline__ bool stage_f16(u32x4 (&xv)[NP], const int (&tok)[NP], int* e) {
+  if (threadIdx.x < 16) e[threadIdx.x] = 0;
+  __syncthreads();
+  int bad = 0;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    if (tok[j] >= 0) {
+      const int em = piece_emax(xv[j], bad);
+      if (em != 0) atomicMax(&e[tok[j]], em);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NP; ++j)
+    if (tok[j] >= 0) bad |= piece_out_of_span(xv[j], e[tok[j]]);
+  const bool f16 = __syncthreads_or(bad) == 0;
+  if (f16) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+      if (tok[j] >= 0) xv[j] = piece_to_f16(xv[j], e[tok[j]]);
+  }
+  return f16;
+}
+
+// Lane (g, i) holds the sums of tokens 4 g + v: their inverse fp16 factors (rows past M carry
+// token M - 1's X, and take its factor).
+__device__ __forceinline__ f32x4 token_unscale(const int* e, int g, int M) {
+  return f32x4{f16_unscale(e[min(4 * g, M - 1)]), f16_unscale(e[min(4 * g + 1, M - 1)]),
+               f16_unscale(e[min(4 * g + 2, M - 1)]), f16_unscale(e[min(4 * g + 3, M - 1)])};
+}
+
+// A weight's tensor scales (one per segment), read once per workgroup. A walking kernel must not
+// read them inside its walk: the epilogue consumes such a load only under a lane mask, which leaves
+// the compiler's wait counters unsure of it and makes it wait for every load in flight (the row
+// tiles prefetched two ahead) at the next reuse of the register.
+static_assert(ATTNQ_MAX_SEGMENTS == 4, "load_tensor_scales holds four segments");
+__device__ __forceinline__ f32x4 load_tensor_scales(const float* __restrict__ ts, int n_seg) {
+  return f32x4{ts[0], n_seg > 1 ? ts[1] : 0.0f, n_seg > 2 ? ts[2] : 0.0f, n_seg > 3 ? ts[3] : 0.0f};
+}
+
+__device__ __forceinline__ float pick_scale(const f32x4& t, int s) { return s == 0 ? t.x : s == 1 ? t.y : s == 2 ? t.z : t.w; }
+
+// One MFMA of the staged-X kernels: X piece xa times 8 codes of word w with block scale s.
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_staged(u32x4 xa, uint32_t w, float s, f16x2 s2, f32x4 acc) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xa), decode8_f16(w, s2), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), decode8_scaled(w, s), acc, 0, 0, 0);
 }
 
 // Tokens-as-rows variant for 4 < M <= 16: A[i][8 g + e] = X[token i][pos] (tokens >= M read as
@@ -556,6 +692,243 @@ __global__ __launch_bounds__(256) void k_gemm_small_m_slices_sum(const float* __
   Y[(size_t)m * ldy + row] = t * tensor_scale[segment_of(segs, row)];
 }
 
+// Walking K strips (k_gemm_small_m_walk): a workgroup of four waves owns one strip of SC chunks
+// (32 SC elements) of K and walks the row groups (64 rows, 16 per wave) with a fixed stride; the
+// grid is what the device holds at once, so there is no second round. The strip's X (tokens up to
+// MT) is staged in LDS once, in fp16 when the window allows it (stage_f16). Each wave keeps the
+// codes and scales of its next two row tiles in flight in two register sets while it turns the
+// current tile into MFMA operands through its LDS tile, with the slices' operand placement. A
+// strip's raw partial sums go to the workspace in the slices' layout and k_gemm_small_m_slices_sum
+// adds them in strip order; a single strip stores Y directly. Strips are whole (SC divides the
+// row's chunks) and 128-byte aligned (SC a multiple of 8), so every cache line of codes is read by
+// one strip.
+//
+// Loads go through buffer resources bounded to the codes' and scales' extents: a load at an offset
+// past the end returns zeros without a memory request (the bounds check covers the whole offset,
+// kept in the VGPR operand). Rows past N and the tiles past the end of a walk (row0 = N) read
+// zeros that way, and so do the lanes with nothing to load, so every lane loads and nothing here
+// branches or clamps: the number of loads in flight is then the same on every path through the
+// walk, which lets the compiler's wait counts leave the tiles loaded ahead in flight. (The
+// launcher keeps (N + 16) K below 2^32, so no offset wraps.)
+template <int SC>
+struct WalkIn {
+  u32x4 cv[8];          // code chunk of rows 2 j + half (one 16-byte chunk per lane)
+  u32x4 sv;             // 8 chunks' scale pairs: row lane / (SC / 8), chunks 8 (lane % (SC / 8)) ..
+};
+
+struct WalkRes {
+  __amdgpu_buffer_rsrc_t codes, scales;
+};
+
+constexpr int kBufNontemporal = 2;        // buffer load cache policy: nt
+constexpr uint32_t kBufOff = 0x80000000u;  // a column offset past any extent
+
+// ccol / scol: the lane's byte offset in a code / scale row (kBufOff for lanes with nothing to load).
+template <int SC>
+__device__ __forceinline__ void walk_loads(WalkIn<SC>& in, const WalkRes& res, int row0, int half, uint32_t ccol,
+                                           int srow, uint32_t scol, uint32_t code_pitch, uint32_t scale_pitch) {
+  const uint32_t co = (uint32_t)(row0 + half) * code_pitch + ccol;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    in.cv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res.codes, (int)(co + 2u * j * code_pitch),
+                                                                               0, kBufNontemporal));
+  in.sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        res.scales, (int)((uint32_t)(row0 + srow) * scale_pitch + scol), 0, 0));
+}
+
+template <int MT, int SC, bool F16>
+__device__ __forceinline__ void walk_tile(WalkIn<SC>& in, uint8_t* __restrict__ ct, uint8_t* __restrict__ st,
+                                          const uint8_t* __restrict__ xwin, const WalkRes& res, const f32x4& tsv,
+                                          const SegTable& segs, float* __restrict__ Y, int ldy, int M, int N, int rg,
+                                          int ahead_rg, int groups, int wave, int lane, uint32_t ccol, int srow,
+                                          uint32_t scol, int sl, int nstrips, uint32_t code_pitch, uint32_t scale_pitch,
+                                          float* ws, f32x4 unscale) {
+  constexpr int kCodePitch = SC * 16 + 16;
+  constexpr int kXPitch = SC * 64 + 16;
+  constexpr int kPieces = SC / 8;
+  const int g = lane >> 4, i = lane & 15, half = lane >> 5, c_lane = lane & 31;
+  // This tile's codes and scales into the wave's LDS tile, then the registers take the tile two
+  // ahead. Lanes past the strip's width write their row's padding slot. The scale tile is
+  // [row][16 (c % 4) + 2 (c / 4)] (pitch 80): the lane's 8 chunks 8 p + k go out as four dwords
+  // (chunks k and k + 4 side by side); lanes without a piece write the spare row 16.
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<u32x4*>(ct + (2 * j + half) * kCodePitch + 16 * min(c_lane, SC)) = in.cv[j];
+  {
+    const int p = lane % kPieces, r = lane < 16 * kPieces ? lane / kPieces : 16;
+    uint8_t* d = st + r * kSlScalePitch + 4 * p;
+    const uint32_t d0 = in.sv.x, d1 = in.sv.y, d2 = in.sv.z, d3 = in.sv.w;
+    *reinterpret_cast<uint32_t*>(d) = (d0 & 0xFFFFu) | (d2 << 16);
+    *reinterpret_cast<uint32_t*>(d + 16) = (d0 >> 16) | (d2 & 0xFFFF0000u);
+    *reinterpret_cast<uint32_t*>(d + 32) = (d1 & 0xFFFFu) | (d3 << 16);
+    *reinterpret_cast<uint32_t*>(d + 48) = (d1 >> 16) | (d3 & 0xFFFF0000u);
+  }
+  walk_loads<SC>(in, res, ahead_rg < groups ? ahead_rg * 64 + 16 * wave : N, half, ccol, srow, scol, code_pitch,
+                 scale_pitch);
+  // The X operands are the same for every row tile: left visible, the compiler hoists their LDS
+  // reads out of the walk and holds all of them in registers, which costs a wave per SIMD. The
+  // empty asm makes the offset opaque, so they are read per tile.
+  int xoff = min(i, M - 1) * kXPitch;
+  asm volatile("" : "+v"(xoff));
+  f32x4 acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) acc[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const u32x4 sc = *reinterpret_cast<const u32x4*>(st + i * kSlScalePitch + 16 * g);
+#pragma unroll
+  for (int q = 0; q < SC / 4; ++q) {
+    const u32x4 cw = *reinterpret_cast<const u32x4*>(ct + i * kCodePitch + 16 * (4 * q + g));
+    const uint8_t* xp = xwin + xoff + 64 * (4 * q + g);
+    const uint32_t sw = word(sc, q >> 1);                             // chunks 4 q + g, 4 q + 4 + g: 2 scales each
+    float s0 = 0.0f, s1 = 0.0f;
+    f16x2 h0 = {}, h1 = {};
+    if constexpr (F16) {
+      const f16x2 h = (q & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)
+                              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+      h0 = f16x2{h.x, h.x};
+      h1 = f16x2{h.y, h.y};
+    } else {
+      const uint32_t sb = sw >> (16 * (q & 1));
+      s0 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0);
+      s1 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 1);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(xp + 16 * d);
+      acc[d] = mfma_staged<F16>(xa, word(cw, d), d < 2 ? s0 : s1, d < 2 ? h0 : h1, acc[d]);
+    }
+  }
+  f32x4 a4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (F16) a4 *= unscale;
+  const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+  const int row = rg * 64 + 16 * wave + i;            // lane (g, i): tokens 4 g + v of this row
+  if (nstrips == 1) {
+    if (row < N) {
+      const float ts = pick_scale(tsv, segment_of(segs, row));
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (4 * g + v < M) Y[(size_t)(4 * g + v) * ldy + row] = a[v] * ts;
+    }
+    return;
+  }
+  // [row group][strip][token][64 rows]. The stores are unconditional, for the same reason as the
+  // loads: a token row past M read token M - 1's X (and takes its fp16 factor), so its sum is the
+  // same value, written to token M - 1's slot.
+  float* part = ws + (size_t)rg * nstrips * M * 64 + 16 * wave + i;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) part[((size_t)sl * M + min(4 * g + v, M - 1)) * 64] = a[v];
+}
+
+// The walk proper: row tiles rg, rg + walkers, ... alternately from register sets A and B, as a
+// counted loop of two tiles and one tile after it. (With exits between the two tiles, the
+// compiler's control flow lets a B tile follow a B tile, and its wait counts then take the A set's
+// loads as not in flight and wait for them too.)
+template <int MT, int SC, bool F16>
+__device__ __forceinline__ void walk_rows(WalkIn<SC>& A, WalkIn<SC>& B, uint8_t* __restrict__ ct,
+                                          uint8_t* __restrict__ st, const uint8_t* __restrict__ xwin,
+                                          const WalkRes& res, const f32x4& tsv, const SegTable& segs,
+                                          float* __restrict__ Y, int ldy, int M, int N, int rg, int walkers, int groups,
+                                          int wave, int lane, uint32_t ccol, int srow, uint32_t scol, int sl,
+                                          int nstrips, uint32_t code_pitch, uint32_t scale_pitch, float* ws,
+                                          f32x4 unscale) {
+  const int n = (groups - rg + walkers - 1) / walkers;
+  int k = 0;
+  for (; k + 1 < n; k += 2) {
+    walk_tile<MT, SC, F16>(A, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
+                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, unscale);
+    rg += walkers;
+    walk_tile<MT, SC, F16>(B, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
+                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, unscale);
+    rg += walkers;
+  }
+  if (k < n)
+    walk_tile<MT, SC, F16>(A, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
+                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, unscale);
+}
+
+template <int MT, int SC>
+__global__ __launch_bounds__(256) void k_gemm_small_m_walk(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           const float* __restrict__ tensor_scale, SegTable segs,
+                                                           const uint16_t* __restrict__ X, int M, int ldx,
+                                                           float* __restrict__ Y, int ldy, int N, int K, int nstrips,
+                                                           int walkers, float* ws) {
+  static_assert(SC % 8 == 0 && SC <= 32, "strips of whole 128-byte lines, at most 32 chunks");
+  constexpr int kCodePitch = SC * 16 + 16;
+  constexpr int kXPitch = SC * 64 + 16;
+  constexpr int kXPieces = MT * SC * 4;                        // 16-byte pieces of the strip's X
+  constexpr int kXPerThread = (kXPieces + 255) / 256;
+  constexpr int kPieces = SC / 8;                              // 16-byte scale pieces per row
+  __shared__ __align__(16) uint8_t ctile[4][16 * kCodePitch];
+  __shared__ __align__(16) uint8_t stile[4][17 * kSlScalePitch];
+  __shared__ __align__(16) uint8_t xwin[MT * kXPitch];
+  __shared__ int xexp[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, c_lane = lane & 31;
+  // Workgroups are dealt to the 8 XCDs round-robin; when the grid is a multiple of 8, XCD x takes
+  // the x-th eighth of the logical order, so the strips of a row group share one L2 (the scale
+  // lines, read 2 SC bytes per strip, are then fetched once).
+  const int b = gridDim.x % 8 == 0 ? (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int sl = b % nstrips;
+  int rg = b / nstrips;                                        // < groups: walkers <= groups
+  const int groups = (N + 63) >> 6;
+  const int c0 = sl * SC;
+  const uint32_t code_pitch = (uint32_t)K >> 1, scale_pitch = (uint32_t)K >> 4;
+  const uint32_t ccol = c_lane < SC ? 16u * (uint32_t)(c0 + c_lane) : kBufOff;
+  const int srow = lane < 16 * kPieces ? lane / kPieces : 0;
+  const uint32_t scol = lane < 16 * kPieces ? 2u * (uint32_t)c0 + 16u * (uint32_t)(lane % kPieces) : kBufOff;
+  const f32x4 tsv = load_tensor_scales(tensor_scale, segs.n_seg);
+  const WalkRes res{__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes), (short)0, (int)((uint32_t)N * code_pitch),
+                                                      0x00020000),
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(scales), (short)0, (int)((uint32_t)N * scale_pitch),
+                                                      0x00020000)};
+
+  // the strip's X: loaded, checked for the fp16 operands and stored to LDS
+  u32x4 xv[kXPerThread];
+  int tok[kXPerThread];
+#pragma unroll
+  for (int j = 0; j < kXPerThread; ++j) {
+    const int pu = (int)threadIdx.x + 256 * j, p = min(pu, kXPieces - 1);
+    const int m = p / (SC * 4), r = p - m * (SC * 4);
+    const int ch = c0 + (r >> 2);
+    const bool ok = m < M;
+    xv[j] = ok ? *reinterpret_cast<const u32x4*>(X + (size_t)m * ldx + ch * 32 + 8 * (r & 3)) : u32x4{0u, 0u, 0u, 0u};
+    tok[j] = (ok && pu < kXPieces) ? m : -1;
+  }
+  const bool f16 = stage_f16(xv, tok, xexp);
+#pragma unroll
+  for (int j = 0; j < kXPerThread; ++j) {
+    const int p = (int)threadIdx.x + 256 * j;
+    if (p < kXPieces) {
+      const int m = p / (SC * 4), r = p - m * (SC * 4);
+      *reinterpret_cast<u32x4*>(xwin + m * kXPitch + 64 * (r >> 2) + 16 * (r & 3)) = xv[j];
+    }
+  }
+  __syncthreads();
+
+  uint8_t* ct = ctile[wave];
+  uint8_t* st = stile[wave];
+  // the register sets are loaded inside each branch: loaded before it, they would be live into both
+  // walks, and the register allocator then gives the kernel far more registers
+  if (f16) {
+    WalkIn<SC> A, B;
+    walk_loads<SC>(A, res, rg * 64 + 16 * wave, half, ccol, srow, scol, code_pitch, scale_pitch);
+    walk_loads<SC>(B, res, rg + walkers < groups ? (rg + walkers) * 64 + 16 * wave : N, half, ccol, srow, scol,
+                   code_pitch, scale_pitch);
+    const f32x4 unscale = token_unscale(xexp, lane >> 4, M);
+    walk_rows<MT, SC, true>(A, B, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, walkers, groups, wave, lane, ccol,
+                            srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, unscale);
+  } else {
+    // the bf16 fallback keeps one row tile ahead in one register set, so that its registers stay
+    // within the fp16 walk's
+    WalkIn<SC> A;
+    walk_loads<SC>(A, res, rg * 64 + 16 * wave, half, ccol, srow, scol, code_pitch, scale_pitch);
+    const f32x4 one{1.0f, 1.0f, 1.0f, 1.0f};
+    for (; rg < groups; rg += walkers)
+      walk_tile<MT, SC, false>(A, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + walkers, groups, wave, lane,
+                               ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, one);
+  }
+}
+
 template <int RT>
 void launch_scaled(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy, int ks,
                    hipStream_t stream) {
@@ -622,23 +995,97 @@ void launch_slices_t(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, fl
 // 12 waves are within 5% of the best configuration for every shape.
 int pick_ks(const attnq_nvfp4& W) { return max(1, min(12, W.K / kSuper)); }
 
+// Launch plan of the walking strips: rows of more than 6144 elements, and weights of at least 16384
+// rows at M > 2, whose rows split into whole strips of 32, 24 or 16 chunks (K = 5376: 7 strips of
+// 24; 16384: 16 of 32); tokens padded to 4, 8 or 16 in the X strip. Measured on the 31B-like
+// gate|up (43008 x 5376, 8 distinct weights in graph replays, the sum kernel included): M = 3
+// 31.8 us and M = 4 33.1 us against 33.4 and 39.3 for the batch-1 walk; at M = 2 the batch-1
+// walk stays (30.0 against 31.1).
+struct WalkPlan {
+  int mt, sc, nstrips, groups;
+};
+
+bool walk_plan(const attnq_nvfp4& W, int M, WalkPlan* p) {
+  if (M < 1 || M > 16 || (W.K <= 6144 && (M <= 2 || W.N < 16384))) return false;
+  if ((int64_t)(W.N + 16) * W.K >= ((int64_t)1 << 32)) return false;    // 32-bit buffer offsets with room for kBufOff
+  const int cpr = W.K / 32;
+  p->sc = cpr % 32 == 0 ? 32 : (cpr % 24 == 0 ? 24 : (cpr % 16 == 0 ? 16 : 0));
+  if (p->sc == 0) return false;                                         // strips must be whole
+  p->mt = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
+  p->nstrips = cpr / p->sc;
+  p->groups = (W.N + 63) / 64;
+  return true;
+}
+
+template <int MT, int SC>
+void launch_walk_t(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy, const WalkPlan& p,
+                   float* ws, hipStream_t stream) {
+  static std::atomic<int> cap[64];
+  SegTable t;
+  t.n_seg = W.n_seg;
+  for (int s = 0; s < ATTNQ_MAX_SEGMENTS; ++s) t.end[s] = (s < W.n_seg) ? W.seg_end[s] : W.N;
+  int dev = 0, c = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) c = cap[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemm_small_m_walk<MT, SC>, 256, 0) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 && cus > 0) {
+      c = per_cu * cus;
+      if (dev >= 0 && dev < 64) cap[dev].store(c, std::memory_order_relaxed);
+    } else {
+      c = 512;
+    }
+  }
+  int walkers = max(1, min(p.groups, c / p.nstrips));
+  for (int d = 0; d < 7 && walkers > 8 && (walkers * p.nstrips) % 8 != 0; ++d) --walkers;   // a grid of whole eighths
+  k_gemm_small_m_walk<MT, SC><<<(unsigned)(p.nstrips * walkers), 256, 0, stream>>>(
+      W.codes, W.scales, W.tensor_scale, t, X, M, ldx, Y, ldy, W.N, W.K, p.nstrips, walkers, ws);
+  if (p.nstrips > 1)
+    k_gemm_small_m_slices_sum<<<dim3((unsigned)((W.N + 255) / 256), (unsigned)M), 256, 0, stream>>>(
+        ws, W.tensor_scale, t, Y, ldy, M, W.N, p.nstrips);
+}
+
+template <int MT>
+void launch_walk_mt(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy, const WalkPlan& p,
+                    float* ws, hipStream_t stream) {
+  if (p.sc == 24) launch_walk_t<MT, 24>(W, X, M, ldx, Y, ldy, p, ws, stream);
+  else if (p.sc == 32) launch_walk_t<MT, 32>(W, X, M, ldx, Y, ldy, p, ws, stream);
+  else launch_walk_t<MT, 16>(W, X, M, ldx, Y, ldy, p, ws, stream);
+}
+
+// The walking strips take weights of at least 16384 rows (gate|up-like: 43008 x 5376 at M = 8,
+// 35.8 against 45.5 us for the slices, the sum kernel included); narrower weights with long rows
+// (down 5376 x 21504: 20.4 against 19.8 us at M = 8 for the product kernel alone, and slower at M = 4
+// and 16) stay on the one-shot slices.
+bool takes_walk(const attnq_nvfp4& W) { return W.N >= 16384; }
+
 }  // namespace
 
 int64_t gemm_small_m_splitk_workspace_bytes(int N, int K, int M) {
   attnq_nvfp4 W{};
   W.N = N;
   W.K = K;
+  if (N == 0) return 0;
+  WalkPlan wp;
+  if (takes_walk(W) && walk_plan(W, M, &wp)) return wp.nstrips == 1 ? 0 : (int64_t)wp.groups * wp.nstrips * M * 64 * 4;
   SlicePlan p;
-  if (N == 0 || !slice_plan(W, M, &p) || p.nslices == 1) return 0;
+  if (!slice_plan(W, M, &p) || p.nslices == 1) return 0;
   return (int64_t)p.groups * p.nslices * M * 64 * 4;
 }
 
 hipError_t launch_gemm_nvfp4_small_m_splitk(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, float* Y, int ldy,
                                             void* ws, hipStream_t stream) {
   if (W.N == 0 || M == 0) return hipSuccess;
+  float* w = static_cast<float*>(ws);
+  WalkPlan wp;
+  if (takes_walk(W) && walk_plan(W, M, &wp)) {
+    if (wp.mt == 4) launch_walk_mt<4>(W, X, M, ldx, Y, ldy, wp, w, stream);
+    else if (wp.mt == 8) launch_walk_mt<8>(W, X, M, ldx, Y, ldy, wp, w, stream);
+    else launch_walk_mt<16>(W, X, M, ldx, Y, ldy, wp, w, stream);
+    return hipGetLastError();
+  }
   SlicePlan p;
   if (!slice_plan(W, M, &p)) return launch_gemm_nvfp4_small_m(W, X, M, ldx, Y, ldy, stream);
-  float* w = static_cast<float*>(ws);
   if (p.mt == 4) launch_slices_t<4, 1>(W, X, M, ldx, Y, ldy, p, w, stream);
   else if (p.mt == 8 && p.s == 2) launch_slices_t<8, 2>(W, X, M, ldx, Y, ldy, p, w, stream);
   else if (p.mt == 8) launch_slices_t<8, 1>(W, X, M, ldx, Y, ldy, p, w, stream);

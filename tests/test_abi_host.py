@@ -75,17 +75,24 @@ def test_splitk_workspace_sizes():
 
 def test_small_m_splitk_workspace_sizes():
     ws = A.attnq_gemm_nvfp4_small_m_splitk_workspace
-    # fp32 partials [row group of 64][slice][token][64 rows]
-    # gate|up 43008 x 5376 at M = 8: 672 groups, 6 steps of 1024 in slices of 2 -> 3
-    assert ws(43008, 5376, 8) == 672 * 3 * 8 * 64 * 4
-    # down 5376 x 21504 at M = 4: 84 groups, 21 one-step slices
-    assert ws(5376, 21504, 4) == 84 * 21 * 4 * 64 * 4
-    # 16384 x 4096 at M = 16: 256 groups, 4 one-step slices
+    # fp32 partials [row group of 64][strip or slice][token][64 rows]
+    # weights of at least 16384 rows walk whole strips of 32, 24 or 16 chunks:
+    # gate|up 43008 x 5376 at M = 8: 672 groups, 168 chunks -> 7 strips of 24
+    assert ws(43008, 5376, 8) == 672 * 7 * 8 * 64 * 4
+    assert ws(43008, 5376, 3) == 672 * 7 * 3 * 64 * 4     # M = 3, 4 walk too on rows of up to 6144
+    # 16384 x 4096 at M = 16: 256 groups, 128 chunks -> 4 strips of 32
     assert ws(16384, 4096, 16) == 256 * 4 * 16 * 64 * 4
+    assert ws(16384, 1024, 8) == 0                     # one strip: Y stored directly
+    assert ws(300000, 4096, 8) == 4688 * 4 * 8 * 64 * 4
+    assert ws(16384, 512 * 3, 2) == 0                  # rows of up to 6144 at M <= 2: the batch-1 walk
+    # rows that do not split into whole strips take the one-shot slices (two steps of 1024 elements
+    # each at 4 < M <= 8 on weights of at least 16384 rows: 129 chunks -> 5 steps -> 3 slices)
+    assert ws(16400, 4096 + 32, 7) == 257 * 3 * 7 * 64 * 4
+    # narrower weights with long rows take the slices: down 5376 x 21504 at M = 4: 84 groups, 21 slices
+    assert ws(5376, 21504, 4) == 84 * 21 * 4 * 64 * 4
+    assert ws(5376, 21504, 8) == 84 * 21 * 8 * 64 * 4
     assert ws(5376, 4096, 16) == 0                     # fewer rows and short rows: the older kernels
     assert ws(6144, 5376, 4) == 0                      # M <= 4 on rows of up to 6144: the batch-1 walk
-    assert ws(16384, 1024, 8) == 0                     # one slice: Y stored directly
-    assert ws(300000, 4096, 8) == 4688 * 2 * 8 * 64 * 4   # 4 steps in slices of 2
     assert ws(0, 4096, 8) == 0 and ws(64, 4096, 0) == 0
     for bad in [(-1, 4096, 8), (64, 48, 8), (64, 4096, 17), (64, 4096, -1)]:
         assert ws(*bad) == -1

@@ -4,7 +4,10 @@ batches of 8), against the float64 oracle with the fp32 bounds of gpu_helpers: e
 (M <= 4 on long rows, 4 < M <= 8 with one- and two-step slices, M <= 16), ragged K (partial steps
 and chunks), ragged row groups, multi-segment weights, bit-identical repeats (the workspace holding
 another call's partials in between), a workspace shared by several shapes, exact one-hot columns,
-and shapes on the batch-1 walk equal to attnq_gemm_nvfp4_small_m."""
+and shapes on the batch-1 walk equal to attnq_gemm_nvfp4_small_m. Weights of at least 16384 rows
+whose rows split into whole strips take the walking strips, with X staged in fp16 when every
+token's window lies within fp16's normal range after a power-of-two scale, and in bf16 otherwise:
+both operand paths are checked, the fallback forced by X values far apart, subnormal or huge."""
 import numpy as np
 import pytest
 import torch
@@ -148,3 +151,67 @@ def test_small_m_splitk_walk_shapes_equal_the_plain_call(A, N, K, M):
     A.attnq_gemm_nvfp4_small_m_splitk(W, X, Y2, None)
     torch.cuda.synchronize()
     assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
+
+
+def _walk_case(A, X, K, what, layer, n=16400):
+    b = inputs.theta_bundle(n, K, 0, cfg=9, layer=layer, proj=0, passthrough=True)
+    M = X.shape[0]
+    say(what)
+    W, seg_end = gpu_quantize(A, [b], K)
+    c, s, t, _ = oracle_quantize([b])
+    ws = A.small_m_workspace(W.N, K, M)
+    assert ws is not None and ws.numel() > 0                 # the walking strips with partial sums
+    Y = torch.full((M, W.N), np.nan, dtype=torch.float32, device="cuda")
+    A.attnq_gemm_nvfp4_small_m_splitk(W, dev(X), Y, ws)
+    torch.cuda.synchronize()
+    Yh, Yr, ad = host(Y), O.gemm_nvfp4_small_m(c, s, t, X, seg_end), O.abs_dot(c, s, t, X, seg_end)
+    for m in range(M):
+        assert_close_products(Yh[m], Yr[m], ad[m], f"{what}: token {m}")
+    return W, c, s, t
+
+
+def _x_with(M, K, layer, edits):
+    X = inputs.activation_bf16(M, K, 9, layer, 3).copy()
+    for (m, k, v) in edits:
+        X[m, k] = v
+    return X
+
+
+# X windows for the two operand paths of the walk (16400 x 5376: 7 strips of 24 chunks):
+# - plain activations (fp16 operands);
+# - a token with one value 2^40 below its largest (the window falls back to bf16 operands);
+# - one value of 2^100 in a token (fallback; that token's sums are huge, the others' are not);
+# - a bf16 subnormal (fallback);
+# - an all-zero token next to ordinary ones (fp16, that token's factor is 1).
+@pytest.mark.parametrize("M", [3, 4, 8, 13])
+def test_small_m_walk_operand_paths(A, M):
+    K = 5376
+    cases = [("plain", []), ("2^-40 value", [(M - 1, 700, 0x2B80)]), ("2^100 value", [(0, 4000, 0x71C0)]),
+             ("bf16 subnormal", [(M // 2, 10, 0x0003)])]
+    for j, (name, edits) in enumerate(cases):
+        _walk_case(A, _x_with(M, K, 77 + j, edits), K, f"small-M walk {name} M {M}", 77)
+    Z = inputs.activation_bf16(M, K, 9, 81, 3).copy()
+    Z[M - 1, :] = 0
+    _walk_case(A, Z, K, f"small-M walk zero token M {M}", 77)
+
+
+def test_small_m_walk_one_hot_columns_are_exact(A):
+    """On the walking strips (fp16 operands with per-token power-of-two factors) one-hot X rows still
+    return the dequantized columns bit for bit."""
+    N, K, M = 16400, 5376, 8
+    b = inputs.theta_bundle(N, K, 0, cfg=9, layer=82, proj=0, passthrough=True)
+    say("small-M walk one-hot")
+    W, _ = gpu_quantize(A, [b], K)
+    c, s, t, _ = oracle_quantize([b])
+    cols = [0, 31, 767, 768, 2000, 4095, 5000, K - 1]
+    X = np.zeros((M, K), np.uint16)
+    for m, k in enumerate(cols):
+        X[m, k] = 0x3F80 if m % 2 == 0 else 0x4C00          # 1.0, and 2^25 (a factor of 2^-10)
+    ws = A.small_m_workspace(N, K, M)
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    A.attnq_gemm_nvfp4_small_m_splitk(W, dev(X), Y, ws)
+    torch.cuda.synchronize()
+    deq32 = O.dequantize_f32(c, s, t)
+    for m, k in enumerate(cols):
+        scale = np.float32(1.0 if m % 2 == 0 else 2.0 ** 25)
+        assert np.array_equal(host(Y)[m], deq32[:, k] * scale), k
