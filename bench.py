@@ -296,10 +296,11 @@ def dominant_kernel_timing(model: Model, reps: int):
 
 def load_path_timing(A, dev, model: Model, reps: int = 1):
     """Rank-16 reconstruct + RTN quantize over all 410 theta bundles (420 segment writes), timed
-    twice: the staged call (attnq_quantize_nvfp4_staged: W_eff rebuilt once into one shared
-    workspace, then quantized from it) and the two-rebuild call (attnq_quantize_nvfp4: the rebuild
-    is formed again in the quantize pass). Returns {"staged": ms, "two_rebuilds": ms}, elements,
-    distinct bundles."""
+    three ways: the batched staged call per layer (attnq_quantize_nvfp4_staged_batch: a layer's seven
+    bundles in three launches, W_eff staged in one shared workspace), the staged call per bundle
+    (attnq_quantize_nvfp4_staged: W_eff rebuilt once, then quantized from it) and the two-rebuild
+    call (attnq_quantize_nvfp4: the rebuild is formed again in the quantize pass). Returns
+    {"staged_batch": ms, "staged": ms, "two_rebuilds": ms}, elements, distinct bundles."""
     from nvfp4_weight_only_rtn_amd import inputs
     r = 16
     bundles = []      # (W, seg, W0, s, U, V)
@@ -327,6 +328,14 @@ def load_path_timing(A, dev, model: Model, reps: int = 1):
     torch.cuda.synchronize()
 
     ws = A.staged_workspace(max(b[2].shape[0] * b[2].shape[1] for b in bundles), 1, r)
+    per_layer = len(bundles) // len(model.layers)            # a layer's bundles, in order
+    layers = [bundles[i:i + per_layer] for i in range(0, len(bundles), per_layer)]
+    batch_ws = torch.empty(max(A.attnq_quantize_nvfp4_staged_batch_workspace([b[2:] for b in lay]) for lay in layers),
+                           dtype=torch.uint8, device=dev)
+
+    def run_batch():
+        for lay in layers:
+            A.attnq_quantize_nvfp4_staged_batch([b[2:] for b in lay], [b[0] for b in lay], [b[1] for b in lay], batch_ws)
 
     def run_staged():
         for (W, i, W0, s, U, V) in bundles:
@@ -336,10 +345,10 @@ def load_path_timing(A, dev, model: Model, reps: int = 1):
         for (W, i, W0, s, U, V) in bundles:
             A.attnq_quantize_nvfp4(W0, s, U, V, W, seg=i)
     out = {}
-    for name, run in (("staged", run_staged), ("two_rebuilds", run_two)):
+    for name, run in (("staged_batch", run_batch), ("staged", run_staged), ("two_rebuilds", run_two)):
         run()                               # warm-up (first-touch of every buffer)
         out[name] = time_steps(run, reps)
-    del bundles, ws
+    del bundles, ws, batch_ws, layers
     torch.cuda.empty_cache()
     return out, elements, distinct
 
@@ -681,9 +690,9 @@ def main():
         # algorithmic bytes per element -- staged: W0 read, W_eff written and read back (2 + 2 + 2),
         # 0.5625 B of codes and scales written; two rebuilds: W0 read twice + 0.5625 B written.
         # Rank-term flops: 2 * 16 per element per rebuild.
-        per = {"staged": (6.5625, 1), "two_rebuilds": (4.5625, 2)}
-        load = {"ms": round(ms["staged"], 3), "call": "attnq_quantize_nvfp4_staged", "elements": elements,
-                "bundles": distinct, "segments": 420}
+        per = {"staged_batch": (6.5625, 1), "staged": (6.5625, 1), "two_rebuilds": (4.5625, 2)}
+        load = {"ms": round(ms["staged_batch"], 3), "call": "attnq_quantize_nvfp4_staged_batch (one call per layer)",
+                "elements": elements, "bundles": distinct, "segments": 420}
         for name, t in ms.items():
             bpe, rebuilds = per[name]
             load[name] = {"ms": round(t, 3), "TBps_algorithmic": round(elements * bpe / (t * 1e-3) / 1e12, 3),

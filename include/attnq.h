@@ -73,6 +73,7 @@ typedef struct attnq_theta {
 } attnq_theta;
 
 #define ATTNQ_MAX_SEGMENTS 4
+#define ATTNQ_MAX_BATCH 8   /* theta bundles per attnq_quantize_nvfp4_staged_batch call */
 #define ATTNQ_LAYOUT_ROW_MAJOR 0
 
 /* An NVFP4 weight [N][K], possibly several projections fused along N ("Q/K/V fusion":
@@ -141,6 +142,31 @@ ATTNQ_API attnq_status attnq_quantize_nvfp4_staged(const attnq_theta* theta, con
 /* Workspace bytes for attnq_quantize_nvfp4_staged on an [N][K] projection of rank r: 2 N K for
  * r > 0 and N, K > 0, else 0. */
 ATTNQ_API int64_t attnq_quantize_nvfp4_staged_workspace(int32_t N, int32_t K, int32_t r);
+
+/* attnq_quantize_nvfp4_staged for `count` (0..ATTNQ_MAX_BATCH) theta bundles at once, e.g. the
+ * projections of one layer at load time ("Throughput", "What quantization actually saves"): bundle i
+ * is quantized into segment segs[i] of dsts[i], each with the single call's result bit for bit.
+ * The work takes three kernels in stream order instead of three per bundle: the tensor-scale slots
+ * are zeroed together, the rank-16 bundles of whole 32 x 128 tiles are rebuilt in one grid (their
+ * tiles cut into equal runs, one per wave), other bundles' amax passes follow one by one, and one
+ * grid quantizes every bundle.
+ * thetas, dsts, segs: host arrays of `count` entries, each validated as attnq_quantize_nvfp4_staged
+ * validates its arguments; no two entries may name the same segment of the same weight.
+ * workspace: caller-owned device memory of at least
+ * attnq_quantize_nvfp4_staged_batch_workspace(thetas, count) bytes (bundle i's W_eff at the sum of
+ * the earlier bundles' 2 N K, each rounded up to 256 bytes), 256-byte aligned, overlapping no
+ * input or output; contents on entry do not matter. NULL is allowed when that size is 0.
+ * Errors: as attnq_quantize_nvfp4_staged for any entry; ATTNQ_ERR_NULL for NULL arrays with
+ * count > 0; ATTNQ_ERR_SHAPE for count outside [0, ATTNQ_MAX_BATCH]; ATTNQ_ERR_SEGMENT for a
+ * segment named twice. Nothing is launched when an error is returned. */
+ATTNQ_API attnq_status attnq_quantize_nvfp4_staged_batch(const attnq_theta* thetas, const attnq_nvfp4* dsts,
+                                                         const int32_t* segs, int32_t count, void* workspace,
+                                                         int64_t workspace_bytes, attnq_stream stream);
+
+/* Workspace bytes for attnq_quantize_nvfp4_staged_batch: the sum over the bundles of
+ * attnq_quantize_nvfp4_staged_workspace(N, K, r), each rounded up to a multiple of 256; -1 for
+ * count outside [0, ATTNQ_MAX_BATCH] or a NULL array with count > 0. */
+ATTNQ_API int64_t attnq_quantize_nvfp4_staged_batch_workspace(const attnq_theta* thetas, int32_t count);
 
 /* y[n] = sum_k x[k] * weight[n][k] for an NVFP4 weight: one kernel that reads codes and
  * scales once and decodes fp4 in registers ("Where GPU time goes": no dequant pass).

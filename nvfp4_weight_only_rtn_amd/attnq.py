@@ -14,6 +14,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnq.so")
 MAX_SEGMENTS = 4
+MAX_BATCH = 8
 LAYOUT_ROW_MAJOR = 0
 ACT_GELU_TANH, ACT_SILU, ACT_IDENTITY = 0, 1, 2
 
@@ -42,6 +43,8 @@ _SIGS = {
     "attnq_reconstruct": [ctypes.POINTER(_Theta), _P, _P],
     "attnq_quantize_nvfp4": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), _I, _P],
     "attnq_quantize_nvfp4_staged": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), _I, _P, ctypes.c_int64, _P],
+    "attnq_quantize_nvfp4_staged_batch": [ctypes.POINTER(_Theta), ctypes.POINTER(_NVFP4), ctypes.POINTER(_I), _I, _P,
+                                          ctypes.c_int64, _P],
     "attnq_gemv_nvfp4": [ctypes.POINTER(_NVFP4), _P, _P, _P],
     "attnq_gemv_nvfp4_splitk": [ctypes.POINTER(_NVFP4), _P, _P, _P, ctypes.c_int64, _P],
     "attnq_gemv_nvfp4_splitk_noalloc": [ctypes.POINTER(_NVFP4), _P, _P, _P],
@@ -59,6 +62,8 @@ _lib.attnq_gemv_nvfp4_lowrank_workspace.argtypes = [_I, _I, _I]
 _lib.attnq_gemv_nvfp4_lowrank_workspace.restype = ctypes.c_int64
 _lib.attnq_quantize_nvfp4_staged_workspace.argtypes = [_I, _I, _I]
 _lib.attnq_quantize_nvfp4_staged_workspace.restype = ctypes.c_int64
+_lib.attnq_quantize_nvfp4_staged_batch_workspace.argtypes = [ctypes.POINTER(_Theta), _I]
+_lib.attnq_quantize_nvfp4_staged_batch_workspace.restype = ctypes.c_int64
 _lib.attnq_gemv_nvfp4_splitk_workspace.argtypes = [_I, _I]
 _lib.attnq_gemv_nvfp4_splitk_workspace.restype = ctypes.c_int64
 _lib.attnq_gemm_nvfp4_small_m_splitk_workspace.argtypes = [_I, _I, _I]
@@ -156,6 +161,30 @@ def attnq_quantize_nvfp4_staged(W0, s, U, V, dst: NVFP4Weight, ws, seg: int = 0,
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.attnq_quantize_nvfp4_staged(ctypes.byref(th), ctypes.byref(dst.desc()), seg, _ptr(ws), nbytes,
                                             _stream(stream)))
+
+
+def _theta_array(bundles):
+    return (_Theta * max(1, len(bundles)))(*[_theta(*b) for b in bundles])
+
+
+def attnq_quantize_nvfp4_staged_batch_workspace(bundles) -> int:
+    """bundles: (W0, s, U, V) tuples."""
+    return int(_lib.attnq_quantize_nvfp4_staged_batch_workspace(_theta_array(bundles), len(bundles)))
+
+
+def staged_batch_workspace(bundles, device="cuda") -> torch.Tensor | None:
+    n = attnq_quantize_nvfp4_staged_batch_workspace(bundles)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def attnq_quantize_nvfp4_staged_batch(bundles, dsts, segs, ws, stream=None) -> None:
+    """bundles: (W0, s, U, V) tuples; bundle i goes into segment segs[i] of dsts[i]."""
+    n = len(bundles)
+    descs = (_NVFP4 * max(1, n))(*[d.desc() for d in dsts])
+    seg_arr = (_I * max(1, n))(*segs)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.attnq_quantize_nvfp4_staged_batch(_theta_array(bundles), descs, seg_arr, n, _ptr(ws), nbytes,
+                                                  _stream(stream)))
 
 
 def attnq_gemv_nvfp4(W: NVFP4Weight, x, y, stream=None) -> None:

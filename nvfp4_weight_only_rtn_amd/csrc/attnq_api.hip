@@ -98,6 +98,48 @@ int64_t attnq_quantize_nvfp4_staged_workspace(int32_t N, int32_t K, int32_t r) {
   return attnq::quantize_staged_workspace_bytes(N, K, r);
 }
 
+int64_t attnq_quantize_nvfp4_staged_batch_workspace(const attnq_theta* thetas, int32_t count) {
+  if (count < 0 || count > ATTNQ_MAX_BATCH || (count > 0 && thetas == nullptr)) return -1;
+  return attnq::quantize_staged_batch_workspace_bytes(thetas, count);
+}
+
+attnq_status attnq_quantize_nvfp4_staged_batch(const attnq_theta* thetas, const attnq_nvfp4* dsts, const int32_t* segs,
+                                               int32_t count, void* workspace, int64_t workspace_bytes,
+                                               attnq_stream stream) {
+  if (count < 0 || count > ATTNQ_MAX_BATCH) return ATTNQ_ERR_SHAPE;
+  if (count == 0) return ATTNQ_OK;
+  if (thetas == nullptr || dsts == nullptr || segs == nullptr) return ATTNQ_ERR_NULL;
+  uint8_t* codes[ATTNQ_MAX_BATCH];
+  uint8_t* scales[ATTNQ_MAX_BATCH];
+  float* slots[ATTNQ_MAX_BATCH];
+  for (int i = 0; i < count; ++i) {
+    const attnq_theta* theta = thetas + i;
+    const attnq_nvfp4* dst = dsts + i;
+    const int32_t seg = segs[i];
+    attnq_status st = check_theta(theta);
+    if (st != ATTNQ_OK) return st;
+    st = check_nvfp4(dst);
+    if (st != ATTNQ_OK) return st;
+    if (theta->K != dst->K) return ATTNQ_ERR_SHAPE;
+    if (seg < 0 || seg >= dst->n_seg) return ATTNQ_ERR_SEGMENT;
+    const int32_t start = seg == 0 ? 0 : dst->seg_end[seg - 1];
+    if (dst->seg_end[seg] - start != theta->N) return ATTNQ_ERR_SEGMENT;
+    codes[i] = dst->codes + (size_t)start * (dst->K / 2);
+    scales[i] = dst->scales + (size_t)start * (dst->K / 16);
+    slots[i] = dst->tensor_scale + seg;
+    for (int k = 0; k < i; ++k)
+      if (slots[k] == slots[i]) return ATTNQ_ERR_SEGMENT;
+  }
+  const int64_t need = attnq::quantize_staged_batch_workspace_bytes(thetas, count);
+  if (need > 0) {
+    if (workspace == nullptr) return ATTNQ_ERR_NULL;
+    if (workspace_bytes < need) return ATTNQ_ERR_SHAPE;
+    if (!aligned(workspace, 256)) return ATTNQ_ERR_ALIGN;
+  }
+  return from_hip(attnq::launch_quantize_staged_batch(thetas, codes, scales, slots, count, workspace,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 attnq_status attnq_gemv_nvfp4(const attnq_nvfp4* W, const uint16_t* x, float* y, attnq_stream stream) {
   attnq_status st = check_nvfp4(W);
   if (st != ATTNQ_OK) return st;

@@ -15,6 +15,11 @@ hipError_t launch_quantize(const attnq_theta& theta, uint8_t* codes, uint8_t* sc
 hipError_t launch_quantize_staged(const attnq_theta& theta, uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                   void* workspace, hipStream_t stream);
 int64_t quantize_staged_workspace_bytes(int32_t N, int32_t K, int32_t r);
+// the staged quantization of count (<= ATTNQ_MAX_BATCH) bundles, bundle i into codes[i], scales[i],
+// tensor_scale[i] (its segment), W_eff at consecutive 256-byte-aligned places of `workspace`
+hipError_t launch_quantize_staged_batch(const attnq_theta* theta, uint8_t* const* codes, uint8_t* const* scales,
+                                        float* const* tensor_scale, int count, void* workspace, hipStream_t stream);
+int64_t quantize_staged_batch_workspace_bytes(const attnq_theta* theta, int count);
 hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, hipStream_t stream);
 // K split across workgroups for rows of 16384 elements or more (other shapes: launch_gemv_nvfp4);
 // ws holds the tickets (zero on entry, zero again on exit) and the partial sums

@@ -191,10 +191,8 @@ __global__ __launch_bounds__(256) void k_amax_r0(Theta t, uint32_t* slot, int64_
   fold_tensor_scale(m, slot);
 }
 
-__global__ __launch_bounds__(256) void k_quantize_r0(Theta t, const uint32_t* __restrict__ slot, uint8_t* __restrict__ codes,
-                                                     uint8_t* __restrict__ scales, int64_t nblocks) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
+__device__ __forceinline__ void quantize_r0_block(const Theta& t, const uint32_t* __restrict__ slot,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t b) {
   const int bpr = t.K / kBlock;
   const int row = (int)(b / bpr), cb = (int)(b % bpr);
   const uint32_t ts_bits = *slot;
@@ -211,6 +209,12 @@ __global__ __launch_bounds__(256) void k_quantize_r0(Theta t, const uint32_t* __
   quantize_block(wp, ts_bits, packed, S);
   __builtin_nontemporal_store(u32x2{packed[0], packed[1]}, cdst);   // written once, not read here again
   __builtin_nontemporal_store((uint8_t)S, sdst);
+}
+
+__global__ __launch_bounds__(256) void k_quantize_r0(Theta t, const uint32_t* __restrict__ slot, uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales, int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b < nblocks) quantize_r0_block(t, slot, codes, scales, b);
 }
 
 // ---------------------------------------------------------------------------------- rank > 0
@@ -679,6 +683,45 @@ __device__ __forceinline__ void pipe_step(const Theta& t, PipeIn& X, const PipeI
   if (stores_weff(PASS)) unstage_weff(lds, out, t.K, tile_row0, j0, lane);
 }
 
+// One walk of a pipe wave over n row tiles of the 128-column strip at j0: tiles rt, rt + stride,
+// ... The loads for tiles past the walk read the first bytes of each matrix instead (live ==
+// false), so the number of loads in flight never depends on the walk's position.
+template <int PASS>
+__device__ __forceinline__ void pipe_walk(const Theta& t, uint32_t* slot, uint8_t* __restrict__ codes,
+                                          uint8_t* __restrict__ scales, uint16_t* __restrict__ out, int j0, int rt,
+                                          int stride, int n, float ts, float six_ts, int lane, uint8_t* lds) {
+  const int m = lane & 31, blk = lane >> 5;
+  const int acol = j0 + 64 * ((m >> 2) & 1) + 16 * blk + 4 * (m >> 3) + (m & 3);
+  const u32x4* va_p = reinterpret_cast<const u32x4*>(t.V + (size_t)acol * 16);
+  const u32x4* vb_p = reinterpret_cast<const u32x4*>(t.V + (size_t)(acol + 32) * 16);
+  const u32x4 va[2] = {va_p[0], va_p[1]};
+  const u32x4 vb[2] = {vb_p[0], vb_p[1]};
+
+  uint32_t mx = 0;
+  // tiles k = 0 .. n-1 of the walk; X and Y alternate between even and odd ones
+  PipeIn X = pipe_loads(t, rt * kTileRows, j0, lane, true);
+  PipeIn Y = pipe_loads(t, (rt + stride) * kTileRows, j0, lane, 1 < n);
+  f32x32 acc0, acc1;
+  chain16(acc0, X.u0, X.u1, va[0], va[1]);
+  // A counted loop of two steps and one step after it. Written with an exit between the two steps,
+  // the loop's control flow lets a Y step follow a Y step; the compiler's wait counts then take the
+  // X set's loads as not in flight, or it swaps the sets by copying registers, and either way the
+  // loads issued two tiles ahead are waited for one tile early.
+  int k = 0;
+  for (; k + 1 < n; k += 2) {
+    pipe_step<PASS>(t, X, Y, acc0, acc1, va, vb, rt * kTileRows, (rt + 2 * stride) * kTileRows, k + 2 < n, j0, lane,
+                    lds, ts, six_ts, mx, codes, scales, out);
+    rt += stride;
+    pipe_step<PASS>(t, Y, X, acc0, acc1, va, vb, rt * kTileRows, (rt + 2 * stride) * kTileRows, k + 3 < n, j0, lane,
+                    lds, ts, six_ts, mx, codes, scales, out);
+    rt += stride;
+  }
+  if (k < n)
+    pipe_step<PASS>(t, X, Y, acc0, acc1, va, vb, rt * kTileRows, (rt + 2 * stride) * kTileRows, false, j0, lane, lds,
+                    ts, six_ts, mx, codes, scales, out);
+  if (takes_amax(PASS)) fold_wave_amax(mx, slot, lane);
+}
+
 template <int PASS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_lowrank_pipe(
     Theta t, uint32_t* slot, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ out,
@@ -686,8 +729,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   const int lane = threadIdx.x;
   const int strip = blockIdx.x % strips;
   const int tiles_r = t.N / kTileRows;
-  const int j0 = strip * kWaveCols;
-  int rt = blockIdx.x / strips;                   // < tiles_r: walkers <= tiles_r
+  const int rt = blockIdx.x / strips;             // < tiles_r: walkers <= tiles_r
 
   float ts = 0.0f, six_ts = 1.0f;
   if (PASS == kPassQuantize) {
@@ -700,34 +742,99 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     ts = __uint_as_float(ts_bits);
     six_ts = ts_bits ? 6.0f * ts : 1.0f;
   }
-
-  const int m = lane & 31, blk = lane >> 5;
-  const int acol = j0 + 64 * ((m >> 2) & 1) + 16 * blk + 4 * (m >> 3) + (m & 3);
-  const u32x4* va_p = reinterpret_cast<const u32x4*>(t.V + (size_t)acol * 16);
-  const u32x4* vb_p = reinterpret_cast<const u32x4*>(t.V + (size_t)(acol + 32) * 16);
-  const u32x4 va[2] = {va_p[0], va_p[1]};
-  const u32x4 vb[2] = {vb_p[0], vb_p[1]};
-
   __shared__ __align__(16) uint8_t lds[kTileRows * kStageRowBytes];
-  uint32_t mx = 0;
-  // tiles rt, rt + walkers, rt + 2*walkers, ... ; X and Y alternate between even and odd ones
-  PipeIn X = pipe_loads(t, rt * kTileRows, j0, lane, true);
-  PipeIn Y = pipe_loads(t, (rt + walkers) * kTileRows, j0, lane, rt + walkers < tiles_r);
-  f32x32 acc0, acc1;
-  chain16(acc0, X.u0, X.u1, va[0], va[1]);
-  for (;;) {
-    int ahead = rt + 2 * walkers;
-    pipe_step<PASS>(t, X, Y, acc0, acc1, va, vb, rt * kTileRows, ahead * kTileRows, ahead < tiles_r, j0, lane, lds, ts,
-                    six_ts, mx, codes, scales, out);
-    rt += walkers;
-    if (rt >= tiles_r) break;
-    ahead = rt + 2 * walkers;
-    pipe_step<PASS>(t, Y, X, acc0, acc1, va, vb, rt * kTileRows, ahead * kTileRows, ahead < tiles_r, j0, lane, lds, ts,
-                    six_ts, mx, codes, scales, out);
-    rt += walkers;
-    if (rt >= tiles_r) break;
-  }
-  if (takes_amax(PASS)) fold_wave_amax(mx, slot, lane);
+  pipe_walk<PASS>(t, slot, codes, scales, out, strip * kWaveCols, rt, walkers, (tiles_r - rt + walkers - 1) / walkers,
+                  ts, six_ts, lane, lds);
+}
+
+// ------------------------------------------------------------------------- batches of bundles
+// The staged quantization of up to kMaxBatch theta bundles in three launches (the slot resets, the
+// rebuild of every whole-tile rank-16 bundle, the quantization of every bundle) instead of three
+// per bundle: a model's loader calls it once per layer. A bundle's result is the single staged
+// call's bit for bit: each element goes through the same arithmetic, and the amax fold is a max.
+constexpr int kMaxBatch = ATTNQ_MAX_BATCH;
+
+// An element of a per-bundle array picked by a wave-uniform index, without dynamic indexing (which
+// would copy the kernel argument to scratch memory).
+template <typename T>
+__device__ __forceinline__ T pick(const T (&a)[kMaxBatch], int i) {
+  T v = a[0];
+#pragma unroll
+  for (int k = 1; k < kMaxBatch; ++k) v = (k == i) ? a[k] : v;
+  return v;
+}
+
+__device__ __forceinline__ Theta pick_theta(const Theta (&a)[kMaxBatch], int i) {
+  Theta v = a[0];
+#pragma unroll
+  for (int k = 1; k < kMaxBatch; ++k)
+    if (k == i) v = a[k];
+  return v;
+}
+
+struct SlotList {
+  uint32_t* slot[kMaxBatch];
+  int n;
+};
+
+__global__ void k_zero_slots(SlotList l) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < l.n) *pick(l.slot, threadIdx.x) = 0u;
+}
+
+// Rebuild pass of the batch: the bundles' grids of the single call (strips x walkers one-wave
+// workgroups each, as many as the device holds at once) laid end to end in one launch. The device
+// runs them in that order, so a bundle's walks start as the previous bundle's finish, without the
+// gap and the ramp of a launch, and each bundle keeps the single call's access pattern (the walkers
+// of all strips on the same row tile at about the same time, so whole rows are read together).
+struct PipeBatch {
+  Theta t[kMaxBatch];
+  uint32_t* slot[kMaxBatch];
+  uint16_t* out[kMaxBatch];
+  int wg_end[kMaxBatch];        // workgroups of bundles 0 .. i
+  int strips[kMaxBatch], walkers[kMaxBatch];
+  int n;
+};
+
+template <int PASS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_lowrank_pipe_batch(PipeBatch b) {
+  static_assert(PASS == kPassAmax || PASS == kPassAmaxStore || PASS == kPassReconstruct, "no quantize pass in a batch");
+  __shared__ __align__(16) uint8_t lds[kTileRows * kStageRowBytes];
+  const int lane = threadIdx.x;
+  const int wg = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxBatch - 1; ++k) i += (k < b.n - 1 && wg >= b.wg_end[k]) ? 1 : 0;
+  const int local = wg - (i ? pick(b.wg_end, i - 1) : 0);
+  const Theta t = pick_theta(b.t, i);
+  const int strips = pick(b.strips, i), walkers = pick(b.walkers, i);
+  const int strip = local % strips, rt = local / strips;
+  const int tiles_r = t.N / kTileRows;
+  pipe_walk<PASS>(t, pick(b.slot, i), nullptr, nullptr, pick(b.out, i), strip * kWaveCols, rt, walkers,
+                  (tiles_r - rt + walkers - 1) / walkers, 0.0f, 1.0f, lane, lds);
+}
+
+// Quantize pass of the batch: every bundle's 16-element blocks in one grid (bundle by bundle, each
+// bundle starting on a workgroup of its own, so that the bundle index is uniform and its picks are
+// scalar), from W_eff in the workspace (rank > 0) or from s and W0 (rank 0), with the bundle's slot
+// as ts.
+struct QuantBatch {
+  Theta t[kMaxBatch];           // rank 0 form: W_eff, or W0 and s
+  const uint32_t* slot[kMaxBatch];
+  uint8_t* codes[kMaxBatch];
+  uint8_t* scales[kMaxBatch];
+  int64_t nblocks[kMaxBatch];
+  int wg_end[kMaxBatch];        // workgroups of bundles 0 .. i
+  int n;
+};
+
+__global__ __launch_bounds__(256) void k_quantize_r0_batch(QuantBatch q) {
+  const int wg = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxBatch - 1; ++k) i += (k < q.n - 1 && wg >= q.wg_end[k]) ? 1 : 0;
+  const int64_t b = (int64_t)(wg - (i ? pick(q.wg_end, i - 1) : 0)) * 256 + threadIdx.x;
+  if (b < pick(q.nblocks, i))
+    quantize_r0_block(pick_theta(q.t, i), pick(q.slot, i), pick(q.codes, i), pick(q.scales, i), b);
 }
 
 Theta to_theta(const attnq_theta& t) { return Theta{t.W0, t.s, t.U, t.V, t.N, t.K, t.r}; }
@@ -807,6 +914,75 @@ hipError_t launch_quantize_staged(const attnq_theta& th, uint8_t* codes, uint8_t
   launch_lowrank<kPassAmaxStore>(t, slot, nullptr, nullptr, weff, stream);
   const Theta staged{weff, nullptr, nullptr, nullptr, t.N, t.K, 0};   // W_eff, passed through
   k_quantize_r0<<<(unsigned)((nblocks + 255) / 256), 256, 0, stream>>>(staged, slot, codes, scales, nblocks);
+  return hipGetLastError();
+}
+
+int64_t quantize_staged_batch_workspace_bytes(const attnq_theta* th, int count) {
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) total += (quantize_staged_workspace_bytes(th[i].N, th[i].K, th[i].r) + 255) / 256 * 256;
+  return total;
+}
+
+hipError_t launch_quantize_staged_batch(const attnq_theta* th, uint8_t* const* codes, uint8_t* const* scales,
+                                        float* const* tensor_scale, int count, void* workspace, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  SlotList slots{};
+  slots.n = count;
+  PipeBatch pb{};
+  QuantBatch qb{};
+  uint16_t* weff[kMaxBatch] = {};
+  int64_t off = 0;
+  int wgs = 0, qwgs = 0;
+  for (int i = 0; i < count; ++i) {
+    const Theta t = to_theta(th[i]);
+    uint32_t* slot = reinterpret_cast<uint32_t*>(tensor_scale[i]);
+    slots.slot[i] = slot;
+    const int64_t need = quantize_staged_workspace_bytes(t.N, t.K, t.r);
+    weff[i] = need > 0 ? reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + off) : nullptr;
+    off += (need + 255) / 256 * 256;
+    const int64_t nblocks = (int64_t)t.N * (t.K / kBlock);
+    if (nblocks > 0) {
+      qwgs += (int)((nblocks + 255) / 256);
+      qb.t[qb.n] = t.r > 0 ? Theta{weff[i], nullptr, nullptr, nullptr, t.N, t.K, 0} : Theta{t.W0, t.s, nullptr, nullptr, t.N, t.K, 0};
+      qb.slot[qb.n] = slot;
+      qb.codes[qb.n] = codes[i];
+      qb.scales[qb.n] = scales[i];
+      qb.nblocks[qb.n] = nblocks;
+      qb.wg_end[qb.n] = qwgs;
+      ++qb.n;
+    }
+    const bool vec = t.r % 8 == 0 && reinterpret_cast<uintptr_t>(t.U) % 16 == 0 && reinterpret_cast<uintptr_t>(t.V) % 16 == 0;
+    if (nblocks > 0 && t.r == 16 && vec && t.N % kTileRows == 0 && t.K % kWaveCols == 0) {
+      static std::atomic<int> cap[64];
+      const int strips = t.K / kWaveCols;
+      const int walkers = max(1, min(t.N / kTileRows, walk_capacity(k_lowrank_pipe_batch<kPassAmaxStore>, cap) / strips));
+      wgs += strips * walkers;
+      pb.t[pb.n] = t;
+      pb.slot[pb.n] = slot;
+      pb.out[pb.n] = weff[i];
+      pb.wg_end[pb.n] = wgs;
+      pb.strips[pb.n] = strips;
+      pb.walkers[pb.n] = walkers;
+      ++pb.n;
+    }
+  }
+  k_zero_slots<<<1, 64, 0, stream>>>(slots);
+  if (pb.n > 0) k_lowrank_pipe_batch<kPassAmaxStore><<<(unsigned)wgs, 64, 0, stream>>>(pb);
+  for (int i = 0; i < count; ++i) {                 // bundles outside the rank-16 batch, one by one
+    const Theta t = to_theta(th[i]);
+    const int64_t nblocks = (int64_t)t.N * (t.K / kBlock);
+    bool in_pb = false;
+    for (int k = 0; k < pb.n; ++k) in_pb |= pb.out[k] == weff[i] && weff[i] != nullptr;
+    if (nblocks == 0 || in_pb) continue;
+    uint32_t* slot = reinterpret_cast<uint32_t*>(tensor_scale[i]);
+    if (t.r > 0) {
+      launch_lowrank<kPassAmaxStore>(t, slot, nullptr, nullptr, weff[i], stream);
+    } else {
+      const int64_t want = (nblocks + 255) / 256;
+      k_amax_r0<<<(unsigned)(want < 4096 ? want : 4096), 256, 0, stream>>>(t, slot, nblocks);
+    }
+  }
+  if (qb.n > 0) k_quantize_r0_batch<<<(unsigned)qwgs, 256, 0, stream>>>(qb);
   return hipGetLastError();
 }
 

@@ -32,7 +32,8 @@ def test_header_declares_every_call():
               "attnq_gemm_nvfp4_small_m", "attnq_gemv_nvfp4_glu", "attnq_gemv_nvfp4_lowrank",
               "attnq_gemv_nvfp4_lowrank_workspace", "attnq_gemv_nvfp4_splitk",
               "attnq_gemv_nvfp4_splitk_workspace", "attnq_gemv_nvfp4_splitk_noalloc", "attnq_read_ceiling",
-              "attnq_gemm_nvfp4_small_m_splitk", "attnq_gemm_nvfp4_small_m_splitk_workspace", "attnq_status_string"]:
+              "attnq_gemm_nvfp4_small_m_splitk", "attnq_gemm_nvfp4_small_m_splitk_workspace", "attnq_status_string",
+              "attnq_quantize_nvfp4_staged_batch", "attnq_quantize_nvfp4_staged_batch_workspace"]:
         assert n in names
 
 
@@ -197,6 +198,48 @@ def test_quantize_staged_validation():
     assert q(ctypes.byref(r4), ctypes.byref(_nv()), 1, FAKE, need, None) == 4      # seg out of range
     assert q(ctypes.byref(_th(r=4)), ctypes.byref(_nv()), 0, FAKE, need, None) == 1  # U, V missing
     assert q(None, ctypes.byref(_nv()), 0, FAKE, need, None) == 1
+
+
+def _th_array(*ths):
+    return (A._Theta * max(1, len(ths)))(*ths)
+
+
+def test_quantize_staged_batch_workspace_sizes():
+    ws = A.raw_library().attnq_quantize_nvfp4_staged_batch_workspace
+    assert ws(_th_array(), 0) == 0
+    # bundle i's W_eff at the sum of the earlier ones, each rounded up to 256 bytes
+    ths = [_th(N=64, K=256, r=16, U=FAKE, V=FAKE), _th(N=3, K=32, r=4, U=FAKE, V=FAKE), _th(N=64, K=64, r=0),
+           _th(N=5376, K=21504, r=16, U=FAKE, V=FAKE)]
+    assert ws(_th_array(*ths), 4) == 2 * 64 * 256 + 256 + 0 + 2 * 5376 * 21504
+    assert ws(_th_array(*ths[2:3]), 1) == 0
+    assert ws(_th_array(*([ths[0]] * 8)), 8) == 8 * 2 * 64 * 256
+    assert ws(_th_array(*([ths[0]] * 9)), 9) == -1           # at most ATTNQ_MAX_BATCH bundles
+    assert ws(None, 2) == -1 and ws(_th_array(), -1) == -1
+
+
+@no_gpu
+def test_quantize_staged_batch_validation():
+    lib = A.raw_library()
+    q = lib.attnq_quantize_nvfp4_staged_batch
+    r4 = _th(r=4, U=FAKE, V=FAKE)
+    need = A.attnq_quantize_nvfp4_staged_workspace(64, 64, 4)
+    segs2 = (ctypes.c_int32 * 2)(0, 1)
+    fused = _nv(N=128, n_seg=2, seg_end=[64, 128])
+    two = (A._NVFP4 * 2)(fused, fused)
+    ths = _th_array(r4, r4)
+    assert q(ths, two, segs2, 0, None, 0, None) == 0                      # nothing to do
+    assert q(ths, two, segs2, 9, FAKE, 1 << 30, None) == 2                 # count above ATTNQ_MAX_BATCH
+    assert q(ths, two, segs2, -1, FAKE, 1 << 30, None) == 2
+    assert q(None, two, segs2, 2, FAKE, 1 << 30, None) == 1
+    assert q(ths, None, segs2, 2, FAKE, 1 << 30, None) == 1
+    assert q(ths, two, None, 2, FAKE, 1 << 30, None) == 1
+    assert q(ths, two, (ctypes.c_int32 * 2)(0, 0), 2, FAKE, 1 << 30, None) == 4   # one segment named twice
+    assert q(ths, two, (ctypes.c_int32 * 2)(0, 2), 2, FAKE, 1 << 30, None) == 4   # seg out of range
+    assert q(ths, two, segs2, 2, None, 2 * need, None) == 1                # rank > 0 needs a workspace
+    assert q(ths, two, segs2, 2, FAKE, 2 * need - 1, None) == 2            # too small
+    assert q(ths, two, segs2, 2, FAKE + 16, 2 * need, None) == 3           # not 256-byte aligned
+    assert q(_th_array(r4, _th(r=4)), two, segs2, 2, FAKE, 1 << 30, None) == 1    # second bundle lacks U, V
+    assert q(_th_array(r4, _th(N=32, r=4, U=FAKE, V=FAKE)), two, segs2, 2, FAKE, 1 << 30, None) == 4  # row count
 
 
 @no_gpu

@@ -198,3 +198,81 @@ def test_rank16_reconstruct_keeps_nan_and_signed_zero_rules(A):
     A.attnq_reconstruct(*[dev(a) for a in b], out)
     torch.cuda.synchronize()
     assert_same_bits(host_u16(out), O.reconstruct(*b), "rank16 W_eff special values")
+
+
+def _single_staged(A, b, K, seg_ends, seg):
+    W = A.NVFP4Weight.empty(seg_ends[-1], K, seg_ends)
+    W.codes.fill_(0x5A)
+    W.scales.fill_(0xA5)
+    A.attnq_quantize_nvfp4_staged(*[dev(a) for a in b], W, A.staged_workspace(b[0].shape[0], K, b[2].shape[1] if b[2] is not None else 0), seg=seg)
+    return W
+
+
+def _run_batch(A, entries, fill=None):
+    """entries: (bundle, weight, seg); returns after the batched call."""
+    bundles = [tuple(dev(a) for a in b) for b, _, _ in entries]
+    ws = A.staged_batch_workspace(bundles)
+    if ws is not None and fill is not None:
+        ws.fill_(fill)
+    A.attnq_quantize_nvfp4_staged_batch(bundles, [W for _, W, _ in entries], [s for _, _, s in entries], ws)
+    torch.cuda.synchronize()
+
+
+def _segment(W, seg):
+    start = 0 if seg == 0 else W.seg_end[seg - 1]
+    return host(W.codes)[start:W.seg_end[seg]], host(W.scales)[start:W.seg_end[seg]], host(W.tensor_scale)[seg:seg + 1]
+
+
+def test_staged_batch_against_oracle_and_single_calls(A):
+    """One batch of eight bundles: rank-16 whole-tile bundles of several shapes (rebuilt in one grid,
+    runs crossing strips and bundles), three of them the segments of one fused weight; a ragged
+    rank-16 bundle, a rank-4 one and a rank-0 one with row scales (each rebuilt on its own); against
+    the oracle and against the single staged call, bit for bit."""
+    qkv = A.NVFP4Weight.empty(384, 384, [256, 320, 384])
+    qkv.codes.fill_(0x5A)
+    qkv.scales.fill_(0xA5)
+    specs = [((256, 384, 16), qkv, 0), ((64, 384, 16), qkv, 1), ((64, 384, 16), qkv, 2), ((352, 640, 16), None, 0),
+             ((32, 128, 16), None, 0), ((200, 320, 16), None, 0), ((96, 256, 4), None, 0), ((64, 256, 0), None, 0)]
+    entries = []
+    for j, ((N, K, r), W, seg) in enumerate(specs):
+        b = inputs.theta_bundle(N, K, r, cfg=9, layer=60, proj=j, uv_sigma=1e-2)    # r = 0: W0 and s
+        if W is None:
+            W = A.NVFP4Weight.empty(N, K)
+            W.codes.fill_(0x5A)
+            W.scales.fill_(0xA5)
+        entries.append((b, W, seg))
+    say("staged batch of 8 bundles")
+    _run_batch(A, entries, fill=0xFF)
+    for j, (b, W, seg) in enumerate(entries):
+        c, sc, ts = _segment(W, seg)
+        oc, osc, ot = O.quantize_segment(O.reconstruct(*b))
+        what = f"batch bundle {j} {b[0].shape}"
+        assert_same_bits(c, oc, what + " codes")
+        assert_same_bits(sc, osc, what + " scales")
+        assert_same_bits(ts.view(np.uint32), np.array([ot], np.float32).view(np.uint32), what + " ts")
+        S = _single_staged(A, b, W.K, W.seg_end, seg)
+        torch.cuda.synchronize()
+        sc2 = _segment(S, seg)
+        assert np.array_equal(c, sc2[0]) and np.array_equal(sc, sc2[1]) and np.array_equal(ts.view(np.uint32), sc2[2].view(np.uint32))
+
+
+def test_staged_batch_layer_like_equals_single_calls(A):
+    """q, k, v (segments of one weight) and o of a 31B-like attention block at rank 16 in one batch,
+    twice (the workspace refilled in between), against the single staged calls bit for bit."""
+    K = 5376
+    qkv = A.NVFP4Weight.empty(6144, K, [4096, 5120, 6144])
+    o = A.NVFP4Weight.empty(5376, 4096)
+    entries = [(inputs.theta_bundle(n, K, 16, cfg=9, layer=61, proj=j, uv_sigma=1e-3), qkv, j)
+               for j, n in enumerate((4096, 1024, 1024))]
+    entries.append((inputs.theta_bundle(5376, 4096, 16, cfg=9, layer=61, proj=3, uv_sigma=1e-3), o, 0))
+    say("staged batch q|k|v + o")
+    _run_batch(A, entries, fill=0x00)
+    first = [_segment(W, seg) for _, W, seg in entries]
+    _run_batch(A, entries, fill=0x7F)
+    for j, (b, W, seg) in enumerate(entries):
+        again = _segment(W, seg)
+        S = _single_staged(A, b, W.K, W.seg_end, seg)
+        torch.cuda.synchronize()
+        single = _segment(S, seg)
+        for x, y, z in zip(first[j], again, single):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)) and np.array_equal(x.view(np.uint8), z.view(np.uint8)), j
