@@ -736,13 +736,48 @@ __device__ __forceinline__ void walk_loads(WalkIn<SC>& in, const WalkRes& res, i
                                         res.scales, (int)((uint32_t)(row0 + srow) * scale_pitch + scol), 0, 0));
 }
 
-template <int MT, int SC, bool F16>
+// One row tile's MFMAs over the strip (codes and scales in the wave's LDS tile, X at xrow), with
+// fp16 or bf16 operands.
+template <int SC, bool F16>
+__device__ __forceinline__ f32x4 strip_mfma(const uint8_t* __restrict__ ct, const uint8_t* __restrict__ xrow,
+                                            const u32x4& sc, int g, int i) {
+  constexpr int kCodePitch = SC * 16 + 16;
+  f32x4 acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) acc[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < SC / 4; ++q) {
+    const u32x4 cw = *reinterpret_cast<const u32x4*>(ct + i * kCodePitch + 16 * (4 * q + g));
+    const uint8_t* xp = xrow + 64 * (4 * q + g);
+    const uint32_t sw = word(sc, q >> 1);                             // chunks 4 q + g, 4 q + 4 + g: 2 scales each
+    float s0 = 0.0f, s1 = 0.0f;
+    f16x2 h0 = {}, h1 = {};
+    if constexpr (F16) {
+      const f16x2 h = (q & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)
+                              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+      h0 = f16x2{h.x, h.x};
+      h1 = f16x2{h.y, h.y};
+    } else {
+      const uint32_t sb = sw >> (16 * (q & 1));
+      s0 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0);
+      s1 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 1);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(xp + 16 * d);
+      acc[d] = mfma_staged<F16>(xa, word(cw, d), d < 2 ? s0 : s1, d < 2 ? h0 : h1, acc[d]);
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+template <int MT, int SC>
 __device__ __forceinline__ void walk_tile(WalkIn<SC>& in, uint8_t* __restrict__ ct, uint8_t* __restrict__ st,
                                           const uint8_t* __restrict__ xwin, const WalkRes& res, const f32x4& tsv,
                                           const SegTable& segs, float* __restrict__ Y, int ldy, int M, int N, int rg,
                                           int ahead_rg, int groups, int wave, int lane, uint32_t ccol, int srow,
                                           uint32_t scol, int sl, int nstrips, uint32_t code_pitch, uint32_t scale_pitch,
-                                          float* ws, f32x4 unscale) {
+                                          float* ws, bool f16, f32x4 unscale) {
   constexpr int kCodePitch = SC * 16 + 16;
   constexpr int kXPitch = SC * 64 + 16;
   constexpr int kPieces = SC / 8;
@@ -770,35 +805,10 @@ __device__ __forceinline__ void walk_tile(WalkIn<SC>& in, uint8_t* __restrict__ 
   // empty asm makes the offset opaque, so they are read per tile.
   int xoff = min(i, M - 1) * kXPitch;
   asm volatile("" : "+v"(xoff));
-  f32x4 acc[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) acc[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const u32x4 sc = *reinterpret_cast<const u32x4*>(st + i * kSlScalePitch + 16 * g);
-#pragma unroll
-  for (int q = 0; q < SC / 4; ++q) {
-    const u32x4 cw = *reinterpret_cast<const u32x4*>(ct + i * kCodePitch + 16 * (4 * q + g));
-    const uint8_t* xp = xwin + xoff + 64 * (4 * q + g);
-    const uint32_t sw = word(sc, q >> 1);                             // chunks 4 q + g, 4 q + 4 + g: 2 scales each
-    float s0 = 0.0f, s1 = 0.0f;
-    f16x2 h0 = {}, h1 = {};
-    if constexpr (F16) {
-      const f16x2 h = (q & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)
-                              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
-      h0 = f16x2{h.x, h.x};
-      h1 = f16x2{h.y, h.y};
-    } else {
-      const uint32_t sb = sw >> (16 * (q & 1));
-      s0 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0);
-      s1 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 1);
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const u32x4 xa = *reinterpret_cast<const u32x4*>(xp + 16 * d);
-      acc[d] = mfma_staged<F16>(xa, word(cw, d), d < 2 ? s0 : s1, d < 2 ? h0 : h1, acc[d]);
-    }
-  }
-  f32x4 a4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  if (F16) a4 *= unscale;
+  // the window's operand type is uniform: one branch per tile
+  const f32x4 a4 = f16 ? strip_mfma<SC, true>(ct, xwin + xoff, sc, g, i) * unscale
+                       : strip_mfma<SC, false>(ct, xwin + xoff, sc, g, i);
   const float a[4] = {a4.x, a4.y, a4.z, a4.w};
   const int row = rg * 64 + 16 * wave + i;            // lane (g, i): tokens 4 g + v of this row
   if (nstrips == 1) {
@@ -822,27 +832,27 @@ __device__ __forceinline__ void walk_tile(WalkIn<SC>& in, uint8_t* __restrict__ 
 // counted loop of two tiles and one tile after it. (With exits between the two tiles, the
 // compiler's control flow lets a B tile follow a B tile, and its wait counts then take the A set's
 // loads as not in flight and wait for them too.)
-template <int MT, int SC, bool F16>
+template <int MT, int SC>
 __device__ __forceinline__ void walk_rows(WalkIn<SC>& A, WalkIn<SC>& B, uint8_t* __restrict__ ct,
                                           uint8_t* __restrict__ st, const uint8_t* __restrict__ xwin,
                                           const WalkRes& res, const f32x4& tsv, const SegTable& segs,
                                           float* __restrict__ Y, int ldy, int M, int N, int rg, int walkers, int groups,
                                           int wave, int lane, uint32_t ccol, int srow, uint32_t scol, int sl,
                                           int nstrips, uint32_t code_pitch, uint32_t scale_pitch, float* ws,
-                                          f32x4 unscale) {
+                                          bool f16, f32x4 unscale) {
   const int n = (groups - rg + walkers - 1) / walkers;
   int k = 0;
   for (; k + 1 < n; k += 2) {
-    walk_tile<MT, SC, F16>(A, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
-                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, unscale);
+    walk_tile<MT, SC>(A, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
+                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, f16, unscale);
     rg += walkers;
-    walk_tile<MT, SC, F16>(B, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
-                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, unscale);
+    walk_tile<MT, SC>(B, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
+                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, f16, unscale);
     rg += walkers;
   }
   if (k < n)
-    walk_tile<MT, SC, F16>(A, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
-                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, unscale);
+    walk_tile<MT, SC>(A, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + 2 * walkers, groups, wave, lane,
+                           ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, f16, unscale);
 }
 
 template <int MT, int SC>
@@ -882,7 +892,8 @@ __global__ __launch_bounds__(256) void k_gemm_small_m_walk(const uint8_t* __rest
                     __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(scales), (short)0, (int)((uint32_t)N * scale_pitch),
                                                       0x00020000)};
 
-  // the strip's X: loaded, checked for the fp16 operands and stored to LDS
+  // the strip's X, then the first two row tiles' weights (all in flight together); X is checked for
+  // the fp16 operands and stored to LDS while the weights arrive (the barriers wait for LDS only)
   u32x4 xv[kXPerThread];
   int tok[kXPerThread];
 #pragma unroll
@@ -894,6 +905,15 @@ __global__ __launch_bounds__(256) void k_gemm_small_m_walk(const uint8_t* __rest
     xv[j] = ok ? *reinterpret_cast<const u32x4*>(X + (size_t)m * ldx + ch * 32 + 8 * (r & 3)) : u32x4{0u, 0u, 0u, 0u};
     tok[j] = (ok && pu < kXPieces) ? m : -1;
   }
+  // (the scheduling barriers keep the two sets' loads in order: a set's last load moved behind the
+  // other set's makes the walk's first wait cover both)
+  WalkIn<SC> A, B;
+  __builtin_amdgcn_sched_barrier(0);
+  walk_loads<SC>(A, res, rg * 64 + 16 * wave, half, ccol, srow, scol, code_pitch, scale_pitch);
+  __builtin_amdgcn_sched_barrier(0);
+  walk_loads<SC>(B, res, rg + walkers < groups ? (rg + walkers) * 64 + 16 * wave : N, half, ccol, srow, scol,
+                 code_pitch, scale_pitch);
+  __builtin_amdgcn_sched_barrier(0);
   const bool f16 = stage_f16(xv, tok, xexp);
 #pragma unroll
   for (int j = 0; j < kXPerThread; ++j) {
@@ -904,29 +924,9 @@ __global__ __launch_bounds__(256) void k_gemm_small_m_walk(const uint8_t* __rest
     }
   }
   __syncthreads();
-
-  uint8_t* ct = ctile[wave];
-  uint8_t* st = stile[wave];
-  // the register sets are loaded inside each branch: loaded before it, they would be live into both
-  // walks, and the register allocator then gives the kernel far more registers
-  if (f16) {
-    WalkIn<SC> A, B;
-    walk_loads<SC>(A, res, rg * 64 + 16 * wave, half, ccol, srow, scol, code_pitch, scale_pitch);
-    walk_loads<SC>(B, res, rg + walkers < groups ? (rg + walkers) * 64 + 16 * wave : N, half, ccol, srow, scol,
-                   code_pitch, scale_pitch);
-    const f32x4 unscale = token_unscale(xexp, lane >> 4, M);
-    walk_rows<MT, SC, true>(A, B, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, walkers, groups, wave, lane, ccol,
-                            srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, unscale);
-  } else {
-    // the bf16 fallback keeps one row tile ahead in one register set, so that its registers stay
-    // within the fp16 walk's
-    WalkIn<SC> A;
-    walk_loads<SC>(A, res, rg * 64 + 16 * wave, half, ccol, srow, scol, code_pitch, scale_pitch);
-    const f32x4 one{1.0f, 1.0f, 1.0f, 1.0f};
-    for (; rg < groups; rg += walkers)
-      walk_tile<MT, SC, false>(A, ct, st, xwin, res, tsv, segs, Y, ldy, M, N, rg, rg + walkers, groups, wave, lane,
-                               ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, one);
-  }
+  const f32x4 unscale = f16 ? token_unscale(xexp, lane >> 4, M) : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+  walk_rows<MT, SC>(A, B, ctile[wave], stile[wave], xwin, res, tsv, segs, Y, ldy, M, N, rg, walkers, groups, wave, lane,
+                    ccol, srow, scol, sl, nstrips, code_pitch, scale_pitch, ws, f16, unscale);
 }
 
 template <int RT>
