@@ -1053,11 +1053,11 @@ void launch_walk_mt(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, flo
   else launch_walk_t<MT, 16>(W, X, M, ldx, Y, ldy, p, ws, stream);
 }
 
-// The walking strips take weights of at least 16384 rows (gate|up-like: 43008 x 5376 at M = 8,
-// 35.8 against 45.5 us for the slices, the sum kernel included); narrower weights with long rows
-// (down 5376 x 21504: 20.4 against 19.8 us at M = 8 for the product kernel alone, and slower at M = 4
-// and 16) stay on the one-shot slices.
-bool takes_walk(const attnq_nvfp4& W) { return W.N >= 16384; }
+// The walking strips take weights of at least 16384 rows (gate|up-like: 43008 x 5376, 34.0 against
+// 45.5 us for the slices at M = 8, sum kernel included) and, at 4 < M <= 8, narrower weights with
+// long rows (down 5376 x 21504: 22.1 against 24.3 us at M = 8); at M <= 4 and M > 8 those stay on
+// the one-shot slices (down 21.0 against 21.2 at M = 4, 24.8 against 25.5 at M = 16).
+bool takes_walk(const attnq_nvfp4& W, int M) { return W.N >= 16384 || (M > 4 && M <= 8); }
 
 }  // namespace
 
@@ -1067,7 +1067,7 @@ int64_t gemm_small_m_splitk_workspace_bytes(int N, int K, int M) {
   W.K = K;
   if (N == 0) return 0;
   WalkPlan wp;
-  if (takes_walk(W) && walk_plan(W, M, &wp)) return wp.nstrips == 1 ? 0 : (int64_t)wp.groups * wp.nstrips * M * 64 * 4;
+  if (takes_walk(W, M) && walk_plan(W, M, &wp)) return wp.nstrips == 1 ? 0 : (int64_t)wp.groups * wp.nstrips * M * 64 * 4;
   SlicePlan p;
   if (!slice_plan(W, M, &p) || p.nslices == 1) return 0;
   return (int64_t)p.groups * p.nslices * M * 64 * 4;
@@ -1078,7 +1078,7 @@ hipError_t launch_gemm_nvfp4_small_m_splitk(const attnq_nvfp4& W, const uint16_t
   if (W.N == 0 || M == 0) return hipSuccess;
   float* w = static_cast<float*>(ws);
   WalkPlan wp;
-  if (takes_walk(W) && walk_plan(W, M, &wp)) {
+  if (takes_walk(W, M) && walk_plan(W, M, &wp)) {
     if (wp.mt == 4) launch_walk_mt<4>(W, X, M, ldx, Y, ldy, wp, w, stream);
     else if (wp.mt == 8) launch_walk_mt<8>(W, X, M, ldx, Y, ldy, wp, w, stream);
     else launch_walk_mt<16>(W, X, M, ldx, Y, ldy, wp, w, stream);

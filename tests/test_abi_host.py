@@ -89,9 +89,11 @@ def test_small_m_splitk_workspace_sizes():
     # rows that do not split into whole strips take the one-shot slices (two steps of 1024 elements
     # each at 4 < M <= 8 on weights of at least 16384 rows: 129 chunks -> 5 steps -> 3 slices)
     assert ws(16400, 4096 + 32, 7) == 257 * 3 * 7 * 64 * 4
-    # narrower weights with long rows take the slices: down 5376 x 21504 at M = 4: 84 groups, 21 slices
+    # narrower weights with long rows: down 5376 x 21504 at M = 4 takes the slices (84 groups, 21
+    # slices), at M = 8 the walk (84 row groups, 21 strips of 32 chunks: the same partial count)
     assert ws(5376, 21504, 4) == 84 * 21 * 4 * 64 * 4
     assert ws(5376, 21504, 8) == 84 * 21 * 8 * 64 * 4
+    assert ws(5376, 21504, 16) == 84 * 21 * 16 * 64 * 4
     assert ws(5376, 4096, 16) == 0                     # fewer rows and short rows: the older kernels
     assert ws(6144, 5376, 4) == 0                      # M <= 4 on rows of up to 6144: the batch-1 walk
     assert ws(0, 4096, 8) == 0 and ws(64, 4096, 0) == 0

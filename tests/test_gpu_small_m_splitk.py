@@ -47,12 +47,14 @@ def _case(A, segs, K, M, layer, what):
 # (segments, K, M): long rows at M <= 4 (21 one-step slices, ragged last step), M = 5..8 with one-step
 # slices and with two-step slices (>= 16384 rows), M = 9..16, K with a partial last step, K a
 # multiple of 1024, row counts of one row, a ragged row group and several groups, segment
-# boundaries inside a group
+# boundaries inside a group; narrower weights with long rows at 4 < M <= 8 that split into whole
+# strips (the walk: 21 strips of 32 chunks, 8 of 32, 17 of 24)
 @pytest.mark.parametrize("segs,K,M", [((300,), 21504, 1), ((129,), 21504 + 32, 4), ((1, 2), 16384, 3),
                                       ((1,), 6144 + 32, 8), ((77,), 8192 + 96, 5), ((1000, 24), 16384 + 32, 8),
                                       ((16384, 16), 1152 + 96, 6), ((8200, 8200), 2048, 8),
                                       ((16400,), 4096 + 32, 7), ((333,), 21504, 16), ((700, 3, 1097), 7168, 13),
-                                      ((64,), 21504, 9), ((5, 6, 7, 8), 12288, 11), ((16383, 2), 3072, 16)])
+                                      ((64,), 21504, 9), ((5, 6, 7, 8), 12288, 11), ((16383, 2), 3072, 16),
+                                      ((300, 77), 21504, 6), ((5,), 8192, 5), ((64,), 12288 + 256 * 3, 7)])
 def test_small_m_splitk_against_oracle(A, segs, K, M):
     _case(A, segs, K, M, 70, f"small-M split-K {segs}x{K} M {M}")
 
@@ -193,6 +195,14 @@ def test_small_m_walk_operand_paths(A, M):
     Z = inputs.activation_bf16(M, K, 9, 81, 3).copy()
     Z[M - 1, :] = 0
     _walk_case(A, Z, K, f"small-M walk zero token M {M}", 77)
+
+
+def test_small_m_walk_narrow_long_rows_operand_paths(A):
+    """A narrower weight with long rows (377 x 21504 at M = 6: 21 strips of 32 chunks, 6 row groups, the
+    last one ragged) on both operand paths."""
+    M, K = 6, 21504
+    for j, (name, edits) in enumerate([("plain", []), ("2^-40 value", [(2, 20000, 0x2B80)])]):
+        _walk_case(A, _x_with(M, K, 83 + j, edits), K, f"small-M walk narrow {name} M {M}", 83, n=377)
 
 
 def test_small_m_walk_one_hot_columns_are_exact(A):
