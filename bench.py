@@ -660,6 +660,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-load-path", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the streams, small-M, C0 and C1 workloads")
+    ap.add_argument("--extra", default="streams,small_m,c0,c1",
+                    help="comma list of the other workloads to time (streams, small_m, c0, c1)")
+    ap.add_argument("--no-machine-state", action="store_true",
+                    help="skip the rocm-smi probes (for runs under a counter-collecting profiler, whose preload "
+                         "would initialise the GPU in the rocm-smi child before it replaces itself)")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -668,9 +673,15 @@ def main():
               "(more GPUs would shard rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    extra = set() if args.no_extra else {w for w in args.extra.split(",") if w}
+    unknown = extra - {"streams", "small_m", "c0", "c1"}
+    if unknown:
+        print(f"unknown --extra workloads: {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
+
     global EAGER
     EAGER = args.eager
-    state = machine_state()                  # before this process touches the GPU
+    state = None if args.no_machine_state else machine_state()    # before this process touches the GPU
     log(f"machine: {state}")
     import nvfp4_weight_only_rtn_amd.attnq as A
     dev = torch.device("cuda:0")
@@ -732,7 +743,7 @@ def main():
     log(f"per projection: {per_proj}; token read ceiling {ceiling_ms:.4f} ms")
 
     streams = small_m = c0 = c1 = None
-    if not args.no_extra:
+    if "streams" in extra:
         log("timing the chained stream (gate|up epilogue feeds down) and the bf16-attention mix")
         glu_ms = graph_timing(model.glu_step, args.warmup, args.steps)
         glu_bytes = model.glu_bytes_per_step()
@@ -761,12 +772,17 @@ def main():
                                "TBps": round(lr_bytes / (lr_ms * 1e-3) / 1e12, 4)},
         }
         log(f"streams: {streams}")
+    if "small_m" in extra:
         small_m = small_m_timing(A, model, max(3, args.steps // 4))
         log(f"small-M: {small_m}")
-        log("single projection 1024x1152 over rotated copies; the 1B-like 26-layer stack")
+    if "c0" in extra:
+        log("single projection 1024x1152 over rotated copies")
         c0 = single_projection_c0(A, dev, args.trials, args.steps)
+        log(f"C0 {c0}")
+    if "c1" in extra:
+        log("the 1B-like 26-layer stack")
         c1 = small_stack_c1(A, dev, args.trials, args.steps)
-        log(f"C0 {c0}; C1 {c1}")
+        log(f"C1 {c1}")
     if args.calibrate_copy:
         calibrate_copy(dev)
 
