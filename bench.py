@@ -384,7 +384,7 @@ def small_m_timing(A, model: Model, steps: int):
 
 def machine_state():
     """Other GPU processes (rocm-smi --showpids) and the clock levels (rocm-smi --showclocks), read
-    before this process touches the GPU: a busy box reads low, so the run records whether it was idle."""
+    before this process touches the GPU: a busy machine reads low, so the run records whether it was idle."""
     import subprocess
     out = {}
     try:
