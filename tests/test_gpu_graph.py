@@ -1,6 +1,6 @@
-"""Graph-capture safety of the library calls: every entry point that enqueues kernels is captured
-once in a hipGraph (torch.cuda.CUDAGraph on a side stream, as the benchmark does) and the graph
-is replayed several times. Between replays the outputs are overwritten with NaN and unrelated
+"""Graph-capture safety of the library calls: every entry point that enqueues kernels (the
+read-ceiling measurement aid aside) is captured once in a hipGraph (torch.cuda.CUDAGraph on a side
+stream, as the benchmark does) and the graph is replayed several times. Between replays the outputs are overwritten with NaN and unrelated
 eager work runs, with synchronizations; after every replay each output must equal the eager
 result bit for bit (every kernel here is deterministic, and no call records a memset).
 """
@@ -66,9 +66,61 @@ def _poison(out):
             t.fill_(0xA5)
 
 
-def test_graph_replays_match_eager(A):
-    say("graph capture of every entry point")
-    run, out, (W, x) = _setup(A)
+def _setup_more(A):
+    """The calls with workspaces, tickets or slot clears: reconstruct, the staged and batched staged
+    quantization (rank-16 whole tiles and a rank-0 bundle), the split-K GEMV with a workspace and on
+    the static scratch, the bf16 GEMV, and the small-M product on walking strips and on K slices."""
+    K = 1152
+    b16 = [inputs.theta_bundle(64, K, 16, cfg=9, layer=84, proj=p) for p in (0, 1)]
+    b0 = inputs.theta_bundle(96, K, 0, cfg=9, layer=84, proj=2)
+    bundles = [tuple(dev(a) for a in b) for b in b16 + [b0]]
+    Wb = A.NVFP4Weight.empty(64 + 64 + 96, K, [64, 128, 224])
+    ws_b = A.staged_batch_workspace(bundles)
+    th = bundles[0]
+    Ws = A.NVFP4Weight.empty(64, K)
+    ws_s = A.staged_workspace(64, K, 16)
+    We = torch.empty((64, K), dtype=torch.bfloat16, device="cuda")
+    Kd = 21504
+    Wd, _ = gpu_quantize(A, [inputs.theta_bundle(64, Kd, 0, cfg=9, layer=85, proj=0, passthrough=True)], Kd)
+    xd = dev(inputs.activation_bf16(1, Kd, 9, 85, 0).reshape(-1))
+    ws_d = A.splitk_workspace(64, Kd)
+    Kw = 8192                                        # 377 rows, M = 6: walking strips (8 of 32 chunks)
+    Ww, _ = gpu_quantize(A, [inputs.theta_bundle(377, Kw, 0, cfg=9, layer=86, proj=0, passthrough=True)], Kw)
+    Xw = dev(inputs.activation_bf16(6, Kw, 9, 86, 6))
+    ws_w = A.small_m_workspace(377, Kw, 6)
+    Kl = 21504 + 32                                  # 129 rows, M = 4: one-shot K slices
+    Wl, _ = gpu_quantize(A, [inputs.theta_bundle(129, Kl, 0, cfg=9, layer=87, proj=0, passthrough=True)], Kl)
+    Xl = dev(inputs.activation_bf16(4, Kl, 9, 87, 4))
+    ws_l = A.small_m_workspace(129, Kl, 4)
+    assert ws_w is not None and ws_l is not None and ws_d is not None
+    Wh = dev(inputs.normal_bf16((300, K), 0.02, 9, 88, 0, inputs.T_W0))
+    xh = dev(inputs.activation_bf16(1, K, 9, 88, 0).reshape(-1))
+    out = {
+        "We": We, "s_codes": Ws.codes, "s_scales": Ws.scales, "s_ts": Ws.tensor_scale,
+        "b_codes": Wb.codes, "b_scales": Wb.scales, "b_ts": Wb.tensor_scale,
+        "yd": torch.empty((64,), dtype=torch.float32, device="cuda"),
+        "yd_na": torch.empty((64,), dtype=torch.float32, device="cuda"),
+        "yh": torch.empty((300,), dtype=torch.float32, device="cuda"),
+        "Yw": torch.empty((6, 377), dtype=torch.float32, device="cuda"),
+        "Yl": torch.empty((4, 129), dtype=torch.float32, device="cuda"),
+    }
+
+    def run():
+        A.attnq_reconstruct(*th, We)
+        A.attnq_quantize_nvfp4_staged(*th, Ws, ws_s, seg=0)
+        A.attnq_quantize_nvfp4_staged_batch(bundles, [Wb, Wb, Wb], [0, 1, 2], ws_b)
+        A.attnq_gemv_nvfp4_splitk(Wd, xd, out["yd"], ws_d)
+        A.attnq_gemv_nvfp4_splitk_noalloc(Wd, xd, out["yd_na"])
+        A.attnq_gemv_bf16(Wh, xh, out["yh"])
+        A.attnq_gemm_nvfp4_small_m_splitk(Ww, Xw, out["Yw"], ws_w)
+        A.attnq_gemm_nvfp4_small_m_splitk(Wl, Xl, out["Yl"], ws_l)
+    return run, out, (Wd, xd)
+
+
+@pytest.mark.parametrize("setup", [_setup, _setup_more], ids=["gemv_glu_lowrank_small_m_quantize", "workspace_calls"])
+def test_graph_replays_match_eager(A, setup):
+    say(f"graph capture: {setup.__name__}")
+    run, out, (W, x) = setup(A)
     run()
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in out.items()}
