@@ -678,18 +678,21 @@ __global__ __launch_bounds__(256) void k_gemm_small_m_slices_sum(const float* __
   if (row >= N) return;
   const int rg = row >> 6, r = row & 63;
   const float* p = part + ((size_t)rg * nslices * M + m) * 64 + r;
+  const float ts = tensor_scale[segment_of(segs, row)];
+  const size_t step = (size_t)M * 64;
+  // up to 32 slices' loads in flight at once (one round trip for every shape the launchers make
+  // below 33 slices), then added in slice order
   float t = 0.0f;
-  int k = 0;
-  for (; k + 4 <= nslices; k += 4) {                     // four loads in flight, added in order
-    const float a0 = p[(size_t)k * M * 64], a1 = p[(size_t)(k + 1) * M * 64];
-    const float a2 = p[(size_t)(k + 2) * M * 64], a3 = p[(size_t)(k + 3) * M * 64];
-    t += a0;
-    t += a1;
-    t += a2;
-    t += a3;
+  for (int k0 = 0; k0 < nslices; k0 += 32) {
+    float a[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      if (k0 + k < nslices) a[k] = p[(size_t)(k0 + k) * step];
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      if (k0 + k < nslices) t += a[k];
   }
-  for (; k < nslices; ++k) t += p[(size_t)k * M * 64];
-  Y[(size_t)m * ldy + row] = t * tensor_scale[segment_of(segs, row)];
+  Y[(size_t)m * ldy + row] = t * ts;
 }
 
 // Walking K strips (k_gemm_small_m_walk): a workgroup of four waves owns one strip of SC chunks
