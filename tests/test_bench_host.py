@@ -1,5 +1,5 @@
-"""Host-side checks of the benchmark script (no GPU): its refusal of more than one GPU, its
-31B-like shapes against the analytic byte counts of that configuration, and the consistency of
+"""Host-side checks of the benchmark script (no GPU): its refusal of more than one GPU and of an
+unknown workload name, its 31B-like shapes against the analytic byte counts of that configuration, and the consistency of
 the HBM-traffic figure it reports with the committed counter summary."""
 import os
 import re
@@ -18,6 +18,14 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_unknown_extra_workload_is_refused_before_the_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--extra", "small_m,nope", "--no-machine-state"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "nope" in r.stderr
     assert r.stdout == ""
 
 
@@ -68,7 +76,8 @@ def test_traffic_figure_matches_the_committed_counter_summary():
 
 
 @pytest.mark.parametrize("name", ["gemv_nvfp4_31b_token_kernel_stats.md", "gemv_nvfp4_31b_token_traffic.md",
-                                  "gemv_nvfp4_31b_token_sq_counters.md"])
+                                  "gemv_nvfp4_31b_token_sq_counters.md", "gemm_small_m_31b_layer_sq_counters.md",
+                                  "quantize_rank16_load_path.md"])
 def test_profile_summaries_name_their_commands(name):
     text = open(os.path.join(ROOT, "profiles", name)).read()
     assert "rocprofv3" in text and "bench.py" in text
