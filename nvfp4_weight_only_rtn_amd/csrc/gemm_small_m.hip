@@ -670,6 +670,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_small_m_slices(const uint8_
 
 // Second kernel of a sliced product (stream order makes the partials visible): thread (m, row) adds
 // the row group's slices in slice order, applies the tensor scale and stores Y[m][row].
+template <int NS>
 __global__ __launch_bounds__(256) void k_gemm_small_m_slices_sum(const float* __restrict__ part,
                                                                  const float* __restrict__ tensor_scale, SegTable segs,
                                                                  float* __restrict__ Y, int ldy, int M, int N,
@@ -680,19 +681,28 @@ __global__ __launch_bounds__(256) void k_gemm_small_m_slices_sum(const float* __
   const float* p = part + ((size_t)rg * nslices * M + m) * 64 + r;
   const float ts = tensor_scale[segment_of(segs, row)];
   const size_t step = (size_t)M * 64;
-  // up to 32 slices' loads in flight at once (one round trip for every shape the launchers make
-  // below 33 slices), then added in slice order
+  // NS slices' loads in flight at once (8 or 32, the launcher's choice by the slice count), then
+  // added in slice order
   float t = 0.0f;
-  for (int k0 = 0; k0 < nslices; k0 += 32) {
-    float a[32];
+  for (int k0 = 0; k0 < nslices; k0 += NS) {
+    float a[NS];
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
+    for (int k = 0; k < NS; ++k)
       if (k0 + k < nslices) a[k] = p[(size_t)(k0 + k) * step];
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
+    for (int k = 0; k < NS; ++k)
       if (k0 + k < nslices) t += a[k];
   }
   Y[(size_t)m * ldy + row] = t * ts;
+}
+
+void launch_slices_sum(const float* part, const float* tensor_scale, const SegTable& t, float* Y, int ldy, int M, int N,
+                       int nslices, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)M);
+  if (nslices <= 8)
+    k_gemm_small_m_slices_sum<8><<<grid, 256, 0, stream>>>(part, tensor_scale, t, Y, ldy, M, N, nslices);
+  else
+    k_gemm_small_m_slices_sum<32><<<grid, 256, 0, stream>>>(part, tensor_scale, t, Y, ldy, M, N, nslices);
 }
 
 // Walking K strips (k_gemm_small_m_walk): a workgroup of four waves owns one strip of SC chunks
@@ -989,8 +999,7 @@ void launch_slices_t(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, fl
   k_gemm_small_m_slices<MT, 4, S><<<(unsigned)(p.groups * p.nslices), 256, 0, stream>>>(
       W.codes, W.scales, W.tensor_scale, t, X, M, ldx, Y, ldy, W.N, W.K, p.nslices, ws);
   if (p.nslices > 1)
-    k_gemm_small_m_slices_sum<<<dim3((unsigned)((W.N + 255) / 256), (unsigned)M), 256, 0, stream>>>(
-        ws, W.tensor_scale, t, Y, ldy, M, W.N, p.nslices);
+    launch_slices_sum(ws, W.tensor_scale, t, Y, ldy, M, W.N, p.nslices, stream);
 }
 
 // K split: 12 waves per workgroup (at most one per superchunk). Timed on MI355X over the
@@ -1044,8 +1053,7 @@ void launch_walk_t(const attnq_nvfp4& W, const uint16_t* X, int M, int ldx, floa
   k_gemm_small_m_walk<MT, SC><<<(unsigned)(p.nstrips * walkers), 256, 0, stream>>>(
       W.codes, W.scales, W.tensor_scale, t, X, M, ldx, Y, ldy, W.N, W.K, p.nstrips, walkers, ws);
   if (p.nstrips > 1)
-    k_gemm_small_m_slices_sum<<<dim3((unsigned)((W.N + 255) / 256), (unsigned)M), 256, 0, stream>>>(
-        ws, W.tensor_scale, t, Y, ldy, M, W.N, p.nstrips);
+    launch_slices_sum(ws, W.tensor_scale, t, Y, ldy, M, W.N, p.nstrips, stream);
 }
 
 template <int MT>
