@@ -665,6 +665,8 @@ def main():
     ap.add_argument("--no-machine-state", action="store_true",
                     help="skip the rocm-smi probes (for runs under a counter-collecting profiler, whose preload "
                          "would initialise the GPU in the rocm-smi child before it replaces itself)")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed token replays for at least this long before the warmup steps")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -694,23 +696,6 @@ def main():
     model.quantize_passthrough(dev)
     log(f"passthrough load {time.perf_counter() - t0:.1f} s")
 
-    load = None
-    if not args.no_load_path:
-        log("timing the rank-16 load path over 410 bundles")
-        ms, elements, distinct = load_path_timing(A, dev, model)
-        # algorithmic bytes per element -- staged: W0 read, W_eff written and read back (2 + 2 + 2),
-        # 0.5625 B of codes and scales written; two rebuilds: W0 read twice + 0.5625 B written.
-        # Rank-term flops: 2 * 16 per element per rebuild.
-        per = {"staged_batch": (6.5625, 1), "staged": (6.5625, 1), "two_rebuilds": (4.5625, 2)}
-        load = {"ms": round(ms["staged_batch"], 3), "call": "attnq_quantize_nvfp4_staged_batch (one call per layer)",
-                "elements": elements, "bundles": distinct, "segments": 420}
-        for name, t in ms.items():
-            bpe, rebuilds = per[name]
-            load[name] = {"ms": round(t, 3), "TBps_algorithmic": round(elements * bpe / (t * 1e-3) / 1e12, 3),
-                          "rank_TFLOPs": round(elements * 32 * rebuilds / (t * 1e-3) / 1e12, 2)}
-        log(f"load path: {load}")
-        model.quantize_passthrough(dev)   # restore the passthrough weights for the stream
-
     for _ in range(args.warmup):
         model.step()
     torch.cuda.synchronize()
@@ -721,6 +706,16 @@ def main():
         run = graph.replay
     else:
         run = model.step
+    # settle: replays for at least --settle-ms before the warmup steps (after the set-up's idle
+    # stretches the token ran about 2.5% slower for its first ~150 ms of replays)
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+        n_settle += 10
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(args.warmup):
         run()
     # trials: each times exactly `steps` replays between synchronizations; the value is the median
@@ -783,6 +778,25 @@ def main():
         log("the 1B-like 26-layer stack")
         c1 = small_stack_c1(A, dev, args.trials, args.steps)
         log(f"C1 {c1}")
+    # last of the GPU timings: after the load path's matrix-core and VALU load the token stream ran
+    # about 2.5% slower for the rest of a run
+    load = None
+    if not args.no_load_path:
+        log("timing the rank-16 load path over 410 bundles")
+        lp_ms, elements, distinct = load_path_timing(A, dev, model)
+        # algorithmic bytes per element -- staged: W0 read, W_eff written and read back (2 + 2 + 2),
+        # 0.5625 B of codes and scales written; two rebuilds: W0 read twice + 0.5625 B written.
+        # Rank-term flops: 2 * 16 per element per rebuild.
+        per = {"staged_batch": (6.5625, 1), "staged": (6.5625, 1), "two_rebuilds": (4.5625, 2)}
+        load = {"ms": round(lp_ms["staged_batch"], 3), "call": "attnq_quantize_nvfp4_staged_batch (one call per layer)",
+                "elements": elements, "bundles": distinct, "segments": 420}
+        for name, t in lp_ms.items():
+            bpe, rebuilds = per[name]
+            load[name] = {"ms": round(t, 3), "TBps_algorithmic": round(elements * bpe / (t * 1e-3) / 1e12, 3),
+                          "rank_TFLOPs": round(elements * 32 * rebuilds / (t * 1e-3) / 1e12, 2)}
+        log(f"load path: {load}")
+        model.quantize_passthrough(dev)   # restore the passthrough weights for the stream
+
     if args.calibrate_copy:
         calibrate_copy(dev)
 
@@ -793,6 +807,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": round(settle_ms, 1), "replays": n_settle,
+                   "what": "untimed token replays before the warmup steps, until the device's rate has settled"},
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
