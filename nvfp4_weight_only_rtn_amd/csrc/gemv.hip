@@ -985,8 +985,10 @@ void launch_splitk_sk(const attnq_nvfp4& W, const uint16_t* x, float* y, uint8_t
 // Launch table (timed per shape on MI355X, 31B-like shapes streamed cold, then A/B inside the
 // token stream): rows of up to 6144 elements use the one-shot kernel with x loaded ahead of the
 // weights (XFIRST: better inside the stream, where each layer's x is cold): the fused gate|up
-// (43008 x 5376) with two rows per wave, q|k|v (6144 x 5376) and o (5376 x 4096, two steps) with
-// one. Long rows (the down projection, K = 21504) use the loop kernel with four rows per wave and
+// (43008 x 5376) with two rows per wave and 8 waves, q|k|v (6144 x 5376) with one row per wave and
+// 4 waves, o (5376 x 4096, two steps) with one row per wave and 8 waves (after the branch-free
+// staging, 8 waves for o and 4 for q|k|v measured 3.087 -> 3.077 ms per token against 4 and 8;
+// 16 waves, two rows per wave for q|k|v and 2 waves for o were slower). Long rows (the down projection, K = 21504) use the loop kernel with four rows per wave and
 // K split over two waves (two row groups per workgroup): inside the token stream this beat
 // splits of 1 and 4, 2 or 8 rows per wave, x staged in LDS, the one-shot kernel and a balanced
 // walk with one workgroup per compute unit.
@@ -997,11 +999,11 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
   if (W.K >= 16384)
     launch_nvfp4_loop<4, 2>(W, x, y, stream);
   else if (cpr <= 128)
-    ok = launch_nvfp4_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, stream);    // K <= 4096: one row per wave, two steps (x: 2 x 256 >= K/8)
+    ok = launch_nvfp4_oneshot<1, 1, 2, true, 8, true, 1>(W, x, y, stream);    // K <= 4096: one row per wave, two steps (x: 512 >= K/8)
   else if (cpr <= 192 && W.N >= 16384)
     ok = launch_nvfp4_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused gate|up 43008x5376 (x: 2 x 512 >= K/8)
   else if (cpr <= 192)
-    ok = launch_nvfp4_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 2 x 512 >= K/8)
+    ok = launch_nvfp4_oneshot<1, 1, 3, true, 4, true, 3>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 3 x 256 >= K/8)
   else
     launch_nvfp4_loop<2, 2>(W, x, y, stream);
   return ok ? hipGetLastError() : hipErrorInvalidValue;
@@ -1077,16 +1079,17 @@ hipError_t launch_gemv_nvfp4_splitk_noalloc(const attnq_nvfp4& W, const uint16_t
   return launch_gemv_nvfp4_splitk(W, x, y, ws, stream);
 }
 
-// Small-M on the batch-1 walk: M = 1 .. 4 tokens and rows of at most 192 chunks, in the batch-1
-// launch shapes (o-like rows of up to 128 chunks: one row per wave, two steps, 4 waves; tall
-// weights: two rows per wave; otherwise one row per wave, 8 waves). Returns false (nothing
-// launched) for other shapes.
+// Small-M on the batch-1 walk: M = 1 .. 4 tokens and rows of at most 192 chunks (o-like rows of up
+// to 128 chunks: one row per wave, two steps, 8 waves; tall weights: two rows per wave; otherwise
+// one row per wave, 8 waves). The x staging of up to 4 tokens (34 KB for o-like rows) holds a
+// compute unit to 4 workgroups, so o-like rows take 8 waves per workgroup, not 4: at M = 4 the
+// 31B-like o measured 7.6 -> 6.4 us per launch. Returns false (nothing launched) for other shapes.
 template <int MT>
 void launch_tokens_mt(const attnq_nvfp4& W, const uint16_t* X, int ldx, float* Y, int ldy, hipStream_t stream) {
   const int cpr = W.K / 32;
   const SegTable t = seg_table(W);
-  if (cpr <= 128)          // x: 2 x 256 pieces >= K / 8
-    k_gemm_nvfp4_tokens<MT, 1, 2, 4, 2><<<(W.N + 3) / 4, 256, 0, stream>>>(W.codes, W.scales, W.tensor_scale, t, X,
+  if (cpr <= 128)          // x: 512 pieces >= K / 8
+    k_gemm_nvfp4_tokens<MT, 1, 2, 8, 1><<<(W.N + 7) / 8, 512, 0, stream>>>(W.codes, W.scales, W.tensor_scale, t, X,
                                                                            ldx, Y, ldy, W.N, W.K);
   else if (W.N >= 16384)   // x: 2 x 512 pieces >= K / 8
     k_gemm_nvfp4_tokens<MT, 2, 3, 8, 2><<<(W.N + 15) / 16, 512, 0, stream>>>(W.codes, W.scales, W.tensor_scale, t,
