@@ -59,7 +59,7 @@ LOWRANK_RANK = 16
 # HBM traffic of one fused gate|up launch from the FETCH_SIZE / WRITE_SIZE passes recorded in
 # profiles/gemv_nvfp4_31b_token_traffic.md (FETCH scaled x1.9999, WRITE x1.0 by a 1 GiB copy).
 # Valid only for the kernel code it was measured on: reported as null once that changes.
-GATE_UP_TRAFFIC = {"sources_sha256_16": "950c98e6893e41b0", "bytes": 130370377}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "d7db4b33e8569d3f", "bytes": 130371401}
 
 
 def gemv_sources_hash() -> str:
@@ -831,7 +831,7 @@ def main():
                                  "(60 x per-layer ceilings + lm_head), each timed back to back over distinct buffers",
                          "token_frac_of_ceiling": round(ceiling_ms / ms, 4)},
         "per_projection": per_proj,
-        "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4_oneshot<2,1,3,true,8,true,2,0> (fused gate|up 43008x5376)",
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_nvfp4_oneshot<2,1,3,true,4,true,3,0> (fused gate|up 43008x5376)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (GATE_UP_TRAFFIC["bytes"] if gemv_sources_hash() == GATE_UP_TRAFFIC["sources_sha256_16"]

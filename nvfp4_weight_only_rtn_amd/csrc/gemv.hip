@@ -711,7 +711,11 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
 }
 
 // bf16 weights, one-shot (rows of at most S x 64 chunks of 8 elements): a wave owns R rows and
-// issues every weight and x load of them (S steps) before computing.
+// issues every weight and x load of them (S steps) before computing. Every step computes (lanes
+// past the row on a clamped chunk, their sum dropped by a select) and a scheduling barrier keeps
+// the loads ahead: with the step guarded, the compiler moved the first step's loads into its
+// branch, behind all the others, and the wave waited for every load before its first dot product
+// (lm_head 389 -> 385 us, the bf16-attention stream -0.02 ms).
 template <int R, int S, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_bf16_oneshot(const uint16_t* __restrict__ W,
                                                                   const uint16_t* __restrict__ x,
@@ -732,21 +736,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_bf16_oneshot(const uint16_t
       wv[s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)row * K) + c);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    if (s * 64 + lane < cpr) {
+    const bool ok = s * 64 + lane < cpr;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float a = acc[r];
-        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].x), as_bf16x2(xv[s].x), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].y), as_bf16x2(xv[s].y), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].z), as_bf16x2(xv[s].z), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].w), as_bf16x2(xv[s].w), a, false);
-        acc[r] = a;
-      }
+    for (int r = 0; r < R; ++r) {
+      float a = acc[r];
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].x), as_bf16x2(xv[s].x), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].y), as_bf16x2(xv[s].y), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].z), as_bf16x2(xv[s].z), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[s][r].w), as_bf16x2(xv[s].w), a, false);
+      acc[r] = ok ? a : acc[r];
     }
   }
   wave_sums<R>(acc);
@@ -944,12 +948,13 @@ void launch_lr_loop(const attnq_nvfp4& W, const uint16_t* x, float* y, const Low
                                                        nullptr, 0, lr);
 }
 
-// gate|up epilogue launches: one row pair per wave, F = N / 2 pairs, x loaded ahead of the weights
+// gate|up epilogue launches: one row pair per wave, 4 waves, F = N / 2 pairs, x loaded ahead of the
+// weights (4 waves measured 3.104 -> 3.084 ms per token in the chained stream against 8)
 template <int S>
 bool launch_glu_oneshot(const attnq_nvfp4& W, const uint16_t* x, uint16_t* h, int act, hipStream_t stream) {
   if (W.K / 32 > S * 64) return false;
-  const unsigned grid = (unsigned)((W.N / 2 + 7) / 8);
-  k_gemv_nvfp4_oneshot<2, 1, S, true, 8, true, 2, 1><<<grid, 512, 0, stream>>>(
+  const unsigned grid = (unsigned)((W.N / 2 + 3) / 4);
+  k_gemv_nvfp4_oneshot<2, 1, S, true, 4, true, 3, 1><<<grid, 256, 0, stream>>>(
       W.codes, W.scales, W.tensor_scale, seg_table(W), x, nullptr, W.N, W.K, h, act);
   return true;
 }
@@ -985,10 +990,11 @@ void launch_splitk_sk(const attnq_nvfp4& W, const uint16_t* x, float* y, uint8_t
 // Launch table (timed per shape on MI355X, 31B-like shapes streamed cold, then A/B inside the
 // token stream): rows of up to 6144 elements use the one-shot kernel with x loaded ahead of the
 // weights (XFIRST: better inside the stream, where each layer's x is cold): the fused gate|up
-// (43008 x 5376) with two rows per wave and 8 waves, q|k|v (6144 x 5376) with one row per wave and
+// (43008 x 5376) with two rows per wave and 4 waves, q|k|v (6144 x 5376) with one row per wave and
 // 4 waves, o (5376 x 4096, two steps) with one row per wave and 8 waves (after the branch-free
-// staging, 8 waves for o and 4 for q|k|v measured 3.087 -> 3.077 ms per token against 4 and 8;
-// 16 waves, two rows per wave for q|k|v and 2 waves for o were slower). Long rows (the down projection, K = 21504) use the loop kernel with four rows per wave and
+// staging, 8 waves for o and 4 for q|k|v measured 3.087 -> 3.077 ms per token against 4 and 8,
+// and 4 waves for gate|up 3.102 -> 3.093 against 8; 16 waves, two rows per wave for q|k|v, one for
+// gate|up and 2 waves for o were slower). Long rows (the down projection, K = 21504) use the loop kernel with four rows per wave and
 // K split over two waves (two row groups per workgroup): inside the token stream this beat
 // splits of 1 and 4, 2 or 8 rows per wave, x staged in LDS, the one-shot kernel and a balanced
 // walk with one workgroup per compute unit.
@@ -1001,7 +1007,7 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
   else if (cpr <= 128)
     ok = launch_nvfp4_oneshot<1, 1, 2, true, 8, true, 1>(W, x, y, stream);    // K <= 4096: one row per wave, two steps (x: 512 >= K/8)
   else if (cpr <= 192 && W.N >= 16384)
-    ok = launch_nvfp4_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, stream);    // fused gate|up 43008x5376 (x: 2 x 512 >= K/8)
+    ok = launch_nvfp4_oneshot<2, 1, 3, true, 4, true, 3>(W, x, y, stream);    // fused gate|up 43008x5376 (x: 3 x 256 >= K/8)
   else if (cpr <= 192)
     ok = launch_nvfp4_oneshot<1, 1, 3, true, 4, true, 3>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 3 x 256 >= K/8)
   else
@@ -1101,7 +1107,9 @@ void launch_tokens_mt(const attnq_nvfp4& W, const uint16_t* X, int ldx, float* Y
 
 // Runtime low-rank product over a shared NVFP4 block: the partial sums of t = V^T x (one
 // workgroup per 16 KB chunk of V and segment), then the streaming GEMV with the s / U t epilogue,
-// in the same launch configurations as the plain GEMV.
+// in the plain GEMV's launch configurations for gate|up (4 waves: the low-rank stream 4.290 ->
+// 4.248 ms against 8) and the long rows; q|k|v and o keep 8 and 4 waves (the plain GEMV's 4 and 8
+// measured the same in the low-rank stream).
 int64_t lowrank_workspace_floats(int K, int n_seg, int r) {
   return r == 0 ? 0 : (int64_t)n_seg * lowrank_parts(K, r) * r;
 }
@@ -1121,7 +1129,7 @@ hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, co
   else if (cpr <= 128)
     ok = launch_lr_oneshot<1, 1, 2, true, 4, true, 2>(W, x, y, lr, stream);
   else if (cpr <= 192 && W.N >= 16384)
-    ok = launch_lr_oneshot<2, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
+    ok = launch_lr_oneshot<2, 1, 3, true, 4, true, 3>(W, x, y, lr, stream);
   else if (cpr <= 192)
     ok = launch_lr_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
   else
