@@ -545,6 +545,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_scaled(const ui
 // Y; a shape of one slice stores Y directly. (Adding the slices in the same launch, by the last
 // workgroup to take a ticket as in the split-K GEMV, measured slower here: the publication's round
 // trips hold each workgroup's 72 KB of LDS, which is what limits how many run per compute unit.)
+// Nothing that uses a load sits in a branch, and scheduling barriers keep X, then the weights,
+// ahead of the staging and everything that waits for a weight behind the barrier: with the X
+// staging store guarded, the compiler moved an X load behind the weight loads and the barrier
+// waited for all of them (down 5376 x 21504 at M = 4: 20.6 -> 19.8 us; at M = 12 and 16 -1.3 us).
 constexpr int kSlStep = 1024;                       // K elements per step
 constexpr int kSlCodePitch = kSlStep / 2 + 16;      // bytes per row of a wave's code tile
 constexpr int kSlScalePitch = 80;                   // bytes per row of a wave's scale tile (64 used)
@@ -571,7 +575,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_small_m_slices(const uint8_
   const int row0 = rg * kRows + 16 * wave;
   const uint32_t code_pitch = (uint32_t)K >> 1, scale_pitch = (uint32_t)K >> 4;
   const int cpr = K >> 5;                                       // 32-element chunks per row
-  const int nsteps = (cpr + 31) >> 5;
   const int st0 = sl * S;
   const int xi = min(i, M - 1);
 
@@ -584,6 +587,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_small_m_slices(const uint8_
     const int m = min(r / (kSlStep / 8), M - 1), e = (st0 + s) * kSlStep + 8 * (r % (kSlStep / 8));
     xv[j] = *reinterpret_cast<const u32x4*>(X + (size_t)m * ldx + min(e, K - 8));
   }
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t crow[8], srow[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -602,17 +606,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_small_m_slices(const uint8_
       sv[s][j] = *reinterpret_cast<const uint16_t*>(scales + (srow[j] + 2u * (uint32_t)c));
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kXPerThread; ++j) {
     const int p = (int)threadIdx.x + j * 64 * WAVES;
-    if (p < kXPieces) {
-      const int s = p / kWinPieces, r = p - s * kWinPieces;
-      const int m = r / (kSlStep / 8), e = (st0 + s) * kSlStep + 8 * (r % (kSlStep / 8));
-      *reinterpret_cast<u32x4*>(&xwin[s][m * kSlXPitch + 16 * (r % (kSlStep / 8))]) =
-          (m < M && e < K) ? xv[j] : u32x4{0u, 0u, 0u, 0u};
-    }
+    const int pc = min(p, kXPieces - 1);
+    const int s = pc / kWinPieces, r = pc - s * kWinPieces;
+    const int m = r / (kSlStep / 8), e = (st0 + s) * kSlStep + 8 * (r % (kSlStep / 8));
+    // pieces past the windows go to the padding of window 0's first row, which is never read
+    const int off = p < kXPieces ? m * kSlXPitch + 16 * (r % (kSlStep / 8)) : 2 * kSlStep;
+    *reinterpret_cast<u32x4*>(&xwin[p < kXPieces ? s : 0][off]) = (m < M && e < K) ? xv[j] : u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);       // nothing that waits for a weight load moves above the barrier
 
   f32x4 acc[4];
 #pragma unroll
@@ -621,9 +627,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_small_m_slices(const uint8_
   uint8_t* st = stile[wave];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
+    // no branch on the step: a step past the row has no valid chunk, so its codes are stored as
+    // zeros and it takes no MFMA (a branch would let the compiler move the weight loads behind the
+    // barrier, into the branch that uses them)
     const int step = st0 + s;
-    if (step < nsteps) {
-      const int nck = min(32, cpr - step * 32);                 // valid chunks in this step
+    {
+      const int nck = min(32, cpr - step * 32);                 // valid chunks in this step (<= 0 past the row)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int row = 2 * j + half;
