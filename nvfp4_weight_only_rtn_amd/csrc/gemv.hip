@@ -561,8 +561,9 @@ __global__ __launch_bounds__(256) void k_clear_words(uint32_t* __restrict__ p, i
 // lane's loads issued at once), every token's x is staged in LDS as [token][quarter][chunk], and a
 // wave decodes the fp4 chunk of each of its R rows once and takes its dot products with all MT
 // tokens. Per block and token the arithmetic is the batch-1 kernel's (dot2 chain, then the E4M3
-// scale by one FMA, the tensor scale last), and the launch shapes are the batch-1 table's, so a
-// token's row equals the batch-1 GEMV of that token bit for bit, whatever M is. The x loads come
+// scale by one FMA, the tensor scale last), and a row is summed as there (one wave per row, lane l
+// on chunks l, l + 64, ..., the same wave reduction; the waves per workgroup do not enter a row's
+// sum), so a token's row equals the batch-1 GEMV of that token bit for bit, whatever M is. The x loads come
 // first and the staging and compute have no branches, for the reason given at the one-shot kernel
 // (pieces past x go to the padding entry, lanes past the row compute on a clamped chunk and a
 // select drops their sum).
