@@ -995,7 +995,12 @@ void launch_splitk_sk(const attnq_nvfp4& W, const uint16_t* x, float* y, uint8_t
 // 4 waves, o (5376 x 4096, two steps) with one row per wave and 8 waves (after the branch-free
 // staging, 8 waves for o and 4 for q|k|v measured 3.087 -> 3.077 ms per token against 4 and 8,
 // and 4 waves for gate|up 3.102 -> 3.093 against 8; 16 waves, two rows per wave for q|k|v, one for
-// gate|up and 2 waves for o were slower). Long rows (the down projection, K = 21504) use the loop kernel with four rows per wave and
+// gate|up and 2 waves for o were slower). Rows of at most 64 chunks (K <= 2048: the 1B-like and
+// 1024 x 1152 shapes) take one step instead of two, which left 92 of every 128 lane loads of a
+// 36-chunk row reloading a clamped chunk, with two rows per wave for tall weights; rows of 193 to
+// 256 chunks (the 1B-like down, K = 6912) take four steps instead of the loop kernel. The 26-layer
+// 1B-like stack measured 0.399 -> 0.329 ms per token, the 1024 x 1152 projection 2.62 -> 2.35 us.
+// Long rows (the down projection, K = 21504) use the loop kernel with four rows per wave and
 // K split over two waves (two row groups per workgroup): inside the token stream this beat
 // splits of 1 and 4, 2 or 8 rows per wave, x staged in LDS, the one-shot kernel and a balanced
 // walk with one workgroup per compute unit.
@@ -1005,12 +1010,18 @@ hipError_t launch_gemv_nvfp4(const attnq_nvfp4& W, const uint16_t* x, float* y, 
   bool ok = true;
   if (W.K >= 16384)
     launch_nvfp4_loop<4, 2>(W, x, y, stream);
+  else if (cpr <= 64 && W.N >= 8192)
+    ok = launch_nvfp4_oneshot<2, 1, 1, true, 4, true, 1>(W, x, y, stream);    // K <= 2048, tall (1B-like gate|up 13824x1152): two rows per wave, one step
+  else if (cpr <= 64)
+    ok = launch_nvfp4_oneshot<1, 1, 1, true, 4, true, 1>(W, x, y, stream);    // K <= 2048: one row per wave, one step (x: 256 >= K/8)
   else if (cpr <= 128)
     ok = launch_nvfp4_oneshot<1, 1, 2, true, 8, true, 1>(W, x, y, stream);    // K <= 4096: one row per wave, two steps (x: 512 >= K/8)
   else if (cpr <= 192 && W.N >= 16384)
     ok = launch_nvfp4_oneshot<2, 1, 3, true, 4, true, 3>(W, x, y, stream);    // fused gate|up 43008x5376 (x: 3 x 256 >= K/8)
   else if (cpr <= 192)
     ok = launch_nvfp4_oneshot<1, 1, 3, true, 4, true, 3>(W, x, y, stream);    // fused q|k|v 6144x5376 (x: 3 x 256 >= K/8)
+  else if (cpr <= 256)
+    ok = launch_nvfp4_oneshot<1, 1, 4, true, 8, true, 2>(W, x, y, stream);    // K <= 8192 (1B-like down 1152x6912): four steps (x: 2 x 512 >= K/8)
   else
     launch_nvfp4_loop<2, 2>(W, x, y, stream);
   return ok ? hipGetLastError() : hipErrorInvalidValue;
@@ -1109,8 +1120,10 @@ void launch_tokens_mt(const attnq_nvfp4& W, const uint16_t* X, int ldx, float* Y
 // Runtime low-rank product over a shared NVFP4 block: the partial sums of t = V^T x (one
 // workgroup per 16 KB chunk of V and segment), then the streaming GEMV with the s / U t epilogue,
 // in the plain GEMV's launch configurations for gate|up (4 waves: the low-rank stream 4.290 ->
-// 4.248 ms against 8) and the long rows; q|k|v and o keep 8 and 4 waves (the plain GEMV's 4 and 8
-// measured the same in the low-rank stream).
+// 4.248 ms against 8), rows of 193 to 256 chunks and the long rows; q|k|v and o keep 8 and 4 waves
+// (the plain GEMV's 4 and 8 measured the same in the low-rank stream), and rows of up to 64 chunks
+// two steps, the second masked. Each row is summed in the plain GEMV's order, so with r = 0 and no
+// s the result equals attnq_gemv_nvfp4's bit for bit.
 int64_t lowrank_workspace_floats(int K, int n_seg, int r) {
   return r == 0 ? 0 : (int64_t)n_seg * lowrank_parts(K, r) * r;
 }
@@ -1133,6 +1146,8 @@ hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, co
     ok = launch_lr_oneshot<2, 1, 3, true, 4, true, 3>(W, x, y, lr, stream);
   else if (cpr <= 192)
     ok = launch_lr_oneshot<1, 1, 3, true, 8, true, 2>(W, x, y, lr, stream);
+  else if (cpr <= 256)
+    ok = launch_lr_oneshot<1, 1, 4, true, 8, true, 2>(W, x, y, lr, stream);
   else
     launch_lr_loop<2, 2>(W, x, y, lr, stream);
   return ok ? hipGetLastError() : hipErrorInvalidValue;

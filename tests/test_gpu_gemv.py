@@ -51,8 +51,8 @@ def test_gemv_small_decoder_layer(A):
 
 
 # shapes chosen to hit every launch configuration, ragged rows and ragged K slices
-@pytest.mark.parametrize("N,K", [(1, 32), (3, 64), (17, 96), (1000, 1152), (4097, 2080), (8193, 4096),
-                                 (513, 8192 + 32), (77, 16384 + 32), (300, 21504)])
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 64), (17, 96), (1000, 1152), (8193, 2048), (4097, 2080), (8193, 4096),
+                                 (100, 6144 + 32), (4099, 8192), (513, 8192 + 32), (77, 16384 + 32), (300, 21504)])
 def test_gemv_ragged_shapes(A, N, K):
     b = inputs.theta_bundle(N, K, 0, cfg=9, layer=30, proj=N, passthrough=True)
     x = inputs.activation_bf16(1, K, 9, 30, N)
