@@ -18,7 +18,7 @@ in which each layer's gate|up launch applies the activation epilogue (attnq_gemv
 and its down projection reads that bf16 output; the coverage-matched mix with the attention
 projections left in bf16 (attnq_gemv_bf16) and the MLP in NVFP4; and the runtime low-rank token,
 26 shared NVFP4 blocks in contiguous bands of layers, each layer applying its own rank-16
-s, U, V in the GEMV epilogue (attnq_gemv_nvfp4_lowrank). Consecutive layers of one band read the
+s, U, V in the GEMV epilogue (attnq_gemv_nvfp4_lowrank_splitk; the down projection on the split-K GEMV). Consecutive layers of one band read the
 same block, so part of that stream's block bytes may come from the last-level cache.
 
 Output: one JSON line (see the design doc for the fields). Options:
@@ -198,17 +198,18 @@ class Model:
                 t = torch.empty(self.A.attnq_gemv_nvfp4_lowrank_workspace(K, len(segs), r), dtype=torch.float32,
                                 device=dev)
                 seed += 3
-                lay[name] = (W, s, U, V, t, x, y)
+                lay[name] = (W, s, U, V, t, x, y, self.A.splitk_workspace(W.N, K, device=dev))
             self.lowrank.append(lay)
 
     def lowrank_step(self):
         """Every projection as shared NVFP4 block + its own low-rank delta, never rebuilt
-        (attnq_gemv_nvfp4_lowrank: the t = V^T x kernel, then the GEMV with the s / U t epilogue)."""
+        (attnq_gemv_nvfp4_lowrank_splitk: the t = V^T x kernel, then the GEMV with the s / U t epilogue,
+        the down projection on the split-K GEMV)."""
         A = self.A
         for lay in self.lowrank:
             for name in PROJ_NAMES:
-                W, s, U, V, t, x, y = lay[name]
-                A.attnq_gemv_nvfp4_lowrank(W, s, U, V, x, t, y)
+                W, s, U, V, t, x, y, sws = lay[name]
+                A.attnq_gemv_nvfp4_lowrank_splitk(W, s, U, V, x, t, sws, y)
         A.attnq_gemv_bf16(self.lm_head, self.x_head, self.y_head)
 
     def lowrank_bytes_per_step(self) -> int:
@@ -218,7 +219,7 @@ class Model:
         total = 0
         for lay in self.lowrank:
             for name in PROJ_NAMES:
-                W, s, U, V, t, x, y = lay[name]
+                W, s, U, V, t, x, y, _ = lay[name]
                 n_seg = len(W.seg_end)
                 total += nvfp4_bytes(W.N, W.K, n_seg) + 2 * W.N + 2 * W.N * r + 2 * n_seg * W.K * r + \
                     2 * W.K * n_seg + 8 * t.numel()
@@ -761,7 +762,8 @@ def main():
                                "TBps": round(mixed_bytes / (mixed_ms * 1e-3) / 1e12, 4)},
             "lowrank_banded": {"what": f"runtime low-rank: {LOWRANK_BANDS} shared NVFP4 blocks in contiguous bands of "
                                        f"layers, per-layer per-segment s, U, V at rank {LOWRANK_RANK} applied in the GEMV "
-                                       "epilogue (attnq_gemv_nvfp4_lowrank, 2 launches per projection), bf16 lm_head",
+                                       "epilogue (attnq_gemv_nvfp4_lowrank_splitk, 2 launches per projection, the down projection on the "
+                                       "split-K GEMV), bf16 lm_head",
                                "ms_per_token": round(lr_ms, 5), "bytes_per_token": lr_bytes,
                                "resident_weight_bytes": lr_resident,
                                "TBps": round(lr_bytes / (lr_ms * 1e-3) / 1e12, 4)},

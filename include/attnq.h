@@ -264,6 +264,26 @@ ATTNQ_API attnq_status attnq_gemv_nvfp4_lowrank(const attnq_nvfp4* W0, const uin
                                       const uint16_t* V, int32_t r, const uint16_t* x, float* ws, float* y,
                                       attnq_stream stream);
 
+/* The runtime low-rank product of attnq_gemv_nvfp4_lowrank (the same per-row definition: "AttnQuant
+ * inference for MAX", "How it works"; the GEMV epilogue as in "GPU and cache acceleration", "Future
+ * work") on the split-K GEMV of attnq_gemv_nvfp4_splitk, for rows of 16384 to 24576 elements (the
+ * down projection's K = 21504, which the plain low-rank call reads with one workgroup per row group):
+ * each K slice adds its share of the row terms sum_i U[n][i mod r] * t_i next to its partial sums,
+ * and the workgroup that arrives last at a tile's ticket adds both in slice order and stores
+ * y = (partial sums) * ts * s + (row terms). Other shapes run attnq_gemv_nvfp4_lowrank, and
+ * split_ws is then not touched. ws: as for attnq_gemv_nvfp4_lowrank. split_ws: caller-owned
+ * device memory of at least attnq_gemv_nvfp4_splitk_workspace(N, K) bytes, 256-byte aligned,
+ * filled with zeros once after allocating it (every call leaves its tickets zero; it may be shared
+ * with attnq_gemv_nvfp4_splitk calls ordered on one stream). The row terms are summed in another
+ * order than in attnq_gemv_nvfp4_lowrank, so the two agree within fp32 rounding; repeated calls
+ * give identical bits. Errors: as attnq_gemv_nvfp4_lowrank, and for split_ws as
+ * attnq_gemv_nvfp4_splitk's ws (ATTNQ_ERR_NULL, ATTNQ_ERR_SHAPE when split_ws_bytes is too small,
+ * ATTNQ_ERR_ALIGN). */
+ATTNQ_API attnq_status attnq_gemv_nvfp4_lowrank_splitk(const attnq_nvfp4* W0, const uint16_t* s, const uint16_t* U,
+                                                       const uint16_t* V, int32_t r, const uint16_t* x, float* ws,
+                                                       void* split_ws, int64_t split_ws_bytes, float* y,
+                                                       attnq_stream stream);
+
 /* Number of fp32 values the workspace of attnq_gemv_nvfp4_lowrank needs for a weight of row length
  * K with n_seg segments at rank r (0 when r == 0), or -1 if K, n_seg or r is out of range. Host
  * only, no GPU call. */

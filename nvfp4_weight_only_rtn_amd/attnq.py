@@ -50,6 +50,7 @@ _SIGS = {
     "attnq_gemv_nvfp4_splitk_noalloc": [ctypes.POINTER(_NVFP4), _P, _P, _P],
     "attnq_gemv_nvfp4_glu": [ctypes.POINTER(_NVFP4), _P, _I, _P, _P],
     "attnq_gemv_nvfp4_lowrank": [ctypes.POINTER(_NVFP4), _P, _P, _P, _I, _P, _P, _P, _P],
+    "attnq_gemv_nvfp4_lowrank_splitk": [ctypes.POINTER(_NVFP4), _P, _P, _P, _I, _P, _P, _P, ctypes.c_int64, _P, _P],
     "attnq_gemv_bf16": [_P, _I, _I, _P, _P, _P],
     "attnq_gemm_nvfp4_small_m": [ctypes.POINTER(_NVFP4), _P, _I, _I, _P, _I, _P],
     "attnq_read_ceiling": [_P, ctypes.c_int64, _P, ctypes.c_int64, _P, _P],
@@ -226,6 +227,16 @@ def attnq_gemv_nvfp4_lowrank(W0: NVFP4Weight, s, U, V, x, ws, y, stream=None) ->
         raise ValueError("attnq_gemv_nvfp4_lowrank: workspace smaller than attnq_gemv_nvfp4_lowrank_workspace()")
     _check(_lib.attnq_gemv_nvfp4_lowrank(ctypes.byref(W0.desc()), _ptr(s, 2), _ptr(U, 2), _ptr(V, 2), r, _ptr(x, 2),
                                          _ptr(ws, 4), _ptr(y, 4), _stream(stream)))
+
+
+def attnq_gemv_nvfp4_lowrank_splitk(W0: NVFP4Weight, s, U, V, x, ws, split_ws, y, stream=None) -> None:
+    r = 0 if U is None else U.shape[1]
+    if r and (ws is None or ws.numel() < attnq_gemv_nvfp4_lowrank_workspace(W0.K, len(W0.seg_end), r)):
+        raise ValueError("attnq_gemv_nvfp4_lowrank_splitk: workspace smaller than attnq_gemv_nvfp4_lowrank_workspace()")
+    nbytes = 0 if split_ws is None else split_ws.numel() * split_ws.element_size()
+    _check(_lib.attnq_gemv_nvfp4_lowrank_splitk(ctypes.byref(W0.desc()), _ptr(s, 2), _ptr(U, 2), _ptr(V, 2), r,
+                                                _ptr(x, 2), _ptr(ws, 4), _ptr(split_ws), nbytes, _ptr(y, 4),
+                                                _stream(stream)))
 
 
 def attnq_gemv_bf16(W, x, y, stream=None) -> None:

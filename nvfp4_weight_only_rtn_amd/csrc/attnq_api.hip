@@ -201,6 +201,26 @@ attnq_status attnq_gemv_nvfp4_lowrank(const attnq_nvfp4* W0, const uint16_t* s, 
   return from_hip(attnq::launch_gemv_nvfp4_lowrank(*W0, s, U, V, r, x, ws, y, static_cast<hipStream_t>(stream)));
 }
 
+attnq_status attnq_gemv_nvfp4_lowrank_splitk(const attnq_nvfp4* W0, const uint16_t* s, const uint16_t* U,
+                                             const uint16_t* V, int32_t r, const uint16_t* x, float* ws,
+                                             void* split_ws, int64_t split_ws_bytes, float* y, attnq_stream stream) {
+  attnq_status st = check_nvfp4(W0);
+  if (st != ATTNQ_OK) return st;
+  if (r < 0 || r > kMaxRank) return ATTNQ_ERR_SHAPE;
+  if (x == nullptr || (y == nullptr && W0->N != 0)) return ATTNQ_ERR_NULL;
+  if (r > 0 && ((U == nullptr && W0->N != 0) || V == nullptr || ws == nullptr)) return ATTNQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, 4) || !aligned(s, 2) || !aligned(U, 2) || !aligned(V, 16))
+    return ATTNQ_ERR_ALIGN;
+  const int64_t need = attnq::gemv_nvfp4_splitk_workspace_bytes(W0->N, W0->K);
+  if (need > 0) {
+    if (split_ws == nullptr) return ATTNQ_ERR_NULL;
+    if (split_ws_bytes < need) return ATTNQ_ERR_SHAPE;
+    if (!aligned(split_ws, 256)) return ATTNQ_ERR_ALIGN;
+  }
+  return from_hip(attnq::launch_gemv_nvfp4_lowrank_splitk(*W0, s, U, V, r, x, ws, split_ws, y,
+                                                          static_cast<hipStream_t>(stream)));
+}
+
 int64_t attnq_gemv_nvfp4_lowrank_workspace(int32_t K, int32_t n_seg, int32_t r) {
   if (K <= 0 || K % 32 != 0 || n_seg < 1 || n_seg > ATTNQ_MAX_SEGMENTS || r < 0 || r > kMaxRank) return -1;
   return attnq::lowrank_workspace_floats(K, n_seg, r);

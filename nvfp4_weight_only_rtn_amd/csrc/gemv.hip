@@ -457,17 +457,24 @@ __device__ __forceinline__ void wait_vector_memory() {
   __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0); expcnt and lgkmcnt left at their maxima
 }
 
-template <int R, int S, int WAVES, int XI, int SK>
+// EPI 2: the runtime low-rank epilogue of attnq_gemv_nvfp4_lowrank. Slice ks also takes its share of
+// the row terms d = sum over i < P r of U[row][i mod r] part[g][i] (i in [ks c, (ks + 1) c), c = ceil(P r
+// / SK), lanes stepping by 64, then the wave sum) and publishes it in slot 1 + SK + ks of the record
+// (so SK <= 6); the finishing workgroup adds the SK shares in slice order and stores
+// y = v ts s + d.
+template <int R, int S, int WAVES, int XI, int SK, int EPI = 0>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_splitk(const uint8_t* __restrict__ codes,
                                                                   const uint8_t* __restrict__ scales,
                                                                   const float* __restrict__ tensor_scale, SegTable segs,
                                                                   const uint16_t* __restrict__ x, float* __restrict__ y,
-                                                                  int N, int K, uint8_t* ws) {
+                                                                  int N, int K, uint8_t* ws, LowRank lr = {}) {
   constexpr int kPitch = S * 64 + 4;          // padded as in the one-shot kernel (conflict-free staging)
   constexpr int kTileRows = WAVES * R;
   static_assert(kTileRows * 4 == kSplitSlotBytes && SK <= kSplitMaxSlices, "a slice's partials fill one slot");
+  static_assert(EPI == 0 || (EPI == 2 && 2 * SK <= kSplitMaxSlices), "the row-term shares fill the slots after the partials");
   __shared__ u32x4 xs[4 * kPitch];
   __shared__ float red[kTileRows];
+  [[maybe_unused]] __shared__ float redd[EPI == 2 ? kTileRows : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tile = blockIdx.x / SK, ks = blockIdx.x - tile * SK;
@@ -527,6 +534,25 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_splitk(const uint8_t*
 #pragma unroll
     for (int r = 0; r < R; ++r) red[wave * R + r] = acc[r];
   }
+  if constexpr (EPI == 2) {
+    const int n = lr.P * lr.r;
+    const int cs = (n + SK - 1) / SK, i_end = min(n, (ks + 1) * cs);
+    float d[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int rw = min(row0 + r, N - 1);
+      const float* pg = lr.part + (size_t)segment_of(segs, rw) * n;
+      const uint16_t* u = lr.U + (size_t)rw * lr.r;
+      float c = 0.0f;
+      for (int i = ks * cs + lane; i < i_end; i += 64) c = __builtin_fmaf(bf16_bits_to_f32(u[i % lr.r]), pg[i], c);
+      d[r] = c;
+    }
+    wave_sums<R>(d);
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) redd[wave * R + r] = d[r];
+    }
+  }
   __syncthreads();
   if (wave != 0) return;
   // wave 0 publishes the tile's partials in the tile's record and takes its ticket
@@ -535,6 +561,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_splitk(const uint8_t*
   uint32_t* ticket = reinterpret_cast<uint32_t*>(ws + (size_t)tile * kSplitRecordBytes);
   float* part = reinterpret_cast<float*>(ws + (size_t)tile * kSplitRecordBytes + kSplitSlotBytes) + lane;
   if (mine) __hip_atomic_store(part + ks * kTileRows, red[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (EPI == 2) {
+    if (mine) __hip_atomic_store(part + (SK + ks) * kTileRows, redd[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   wait_vector_memory();                                    // the partial stores have completed
   uint32_t arrived = 0u;
@@ -547,7 +576,15 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_nvfp4_splitk(const uint8_t*
 #pragma unroll
     for (int k2 = 1; k2 < SK; ++k2)
       v += __hip_atomic_load(part + k2 * kTileRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    y[row] = v * tensor_scale[segment_of(segs, row)];
+    if constexpr (EPI == 2) {
+      float dd = __hip_atomic_load(part + SK * kTileRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int k2 = 1; k2 < SK; ++k2)
+        dd += __hip_atomic_load(part + (SK + k2) * kTileRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      y[row] = lr_finish(v, tensor_scale[segment_of(segs, row)], lr, lr.s != nullptr ? lr.s[row] : 0u, dd);
+    } else {
+      y[row] = v * tensor_scale[segment_of(segs, row)];
+    }
   }
   if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -978,12 +1015,13 @@ int splitk_slices(int K) {
   return (slice <= kSplitS * 64 && (sk - 1) * slice < cpr) ? sk : 0;
 }
 
-template <int SK>
-void launch_splitk_sk(const attnq_nvfp4& W, const uint16_t* x, float* y, uint8_t* ws, hipStream_t stream) {
+template <int SK, int EPI = 0>
+void launch_splitk_sk(const attnq_nvfp4& W, const uint16_t* x, float* y, uint8_t* ws, hipStream_t stream,
+                      const LowRank& lr = {}) {
   const unsigned tiles = (unsigned)((W.N + kSplitRows - 1) / kSplitRows);
   constexpr int kXI = (4 * kSplitS * 64 + 64 * kSplitWaves - 1) / (64 * kSplitWaves);   // x pieces per thread
-  k_gemv_nvfp4_splitk<kSplitR, kSplitS, kSplitWaves, kXI, SK><<<tiles * SK, 64 * kSplitWaves, 0, stream>>>(
-      W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K, ws);
+  k_gemv_nvfp4_splitk<kSplitR, kSplitS, kSplitWaves, kXI, SK, EPI><<<tiles * SK, 64 * kSplitWaves, 0, stream>>>(
+      W.codes, W.scales, W.tensor_scale, seg_table(W), x, y, W.N, W.K, ws, lr);
 }
 
 }  // namespace
@@ -1151,6 +1189,32 @@ hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, co
   else
     launch_lr_loop<2, 2>(W, x, y, lr, stream);
   return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+// The low-rank product with the split-K GEMV: rows split into at most 6 K slices (16384 to 24576
+// elements: the 31B-like down projection), whose records hold the row-term shares next to the
+// partial sums; other shapes run launch_gemv_nvfp4_lowrank. The row terms are summed in another
+// order than there (slices of i instead of the wave's K split), so the two agree within fp32
+// rounding, not bit for bit.
+hipError_t launch_gemv_nvfp4_lowrank_splitk(const attnq_nvfp4& W, const uint16_t* s, const uint16_t* U,
+                                            const uint16_t* V, int r, const uint16_t* x, float* ws, void* split_ws,
+                                            float* y, hipStream_t stream) {
+  if (W.N == 0) return hipSuccess;
+  const int sk = splitk_slices(W.K);
+  if (sk == 0 || 2 * sk > kSplitMaxSlices) return launch_gemv_nvfp4_lowrank(W, s, U, V, r, x, ws, y, stream);
+  LowRank lr{s, U, ws, r, 0};
+  if (r > 0) {
+    lr.P = lowrank_parts(W.K, r);
+    launch_lowrank_part(V, x, ws, W.K, r, lr.P, W.n_seg, stream);
+  }
+  uint8_t* w = static_cast<uint8_t*>(split_ws);
+  switch (sk) {
+    case 4: launch_splitk_sk<4, 2>(W, x, y, w, stream, lr); break;
+    case 5: launch_splitk_sk<5, 2>(W, x, y, w, stream, lr); break;
+    case 6: launch_splitk_sk<6, 2>(W, x, y, w, stream, lr); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // gate|up with its activation: the one-shot kernel stages x in LDS for rows of up to 6144

@@ -32,6 +32,9 @@ hipError_t launch_gemv_nvfp4_glu(const attnq_nvfp4& W, const uint16_t* x, int ac
 hipError_t launch_gemv_nvfp4_lowrank(const attnq_nvfp4& W, const uint16_t* s, const uint16_t* U, const uint16_t* V,
                                      int r, const uint16_t* x, float* ws, float* y, hipStream_t stream);
 int64_t lowrank_workspace_floats(int K, int n_seg, int r);
+hipError_t launch_gemv_nvfp4_lowrank_splitk(const attnq_nvfp4& W, const uint16_t* s, const uint16_t* U,
+                                            const uint16_t* V, int r, const uint16_t* x, float* ws, void* split_ws,
+                                            float* y, hipStream_t stream);
 // streaming read of two byte ranges (multiples of 16 bytes), nothing written: the read ceiling
 hipError_t launch_read_ceiling(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes, uint32_t* sink,
                                hipStream_t stream);

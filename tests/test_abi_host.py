@@ -30,7 +30,7 @@ def test_header_declares_every_call():
     for n in ["attnq_reconstruct", "attnq_quantize_nvfp4", "attnq_quantize_nvfp4_staged",
               "attnq_quantize_nvfp4_staged_workspace", "attnq_gemv_nvfp4", "attnq_gemv_bf16",
               "attnq_gemm_nvfp4_small_m", "attnq_gemv_nvfp4_glu", "attnq_gemv_nvfp4_lowrank",
-              "attnq_gemv_nvfp4_lowrank_workspace", "attnq_gemv_nvfp4_splitk",
+              "attnq_gemv_nvfp4_lowrank_workspace", "attnq_gemv_nvfp4_lowrank_splitk", "attnq_gemv_nvfp4_splitk",
               "attnq_gemv_nvfp4_splitk_workspace", "attnq_gemv_nvfp4_splitk_noalloc", "attnq_read_ceiling",
               "attnq_gemm_nvfp4_small_m_splitk", "attnq_gemm_nvfp4_small_m_splitk_workspace", "attnq_status_string",
               "attnq_quantize_nvfp4_staged_batch", "attnq_quantize_nvfp4_staged_batch_workspace"]:
@@ -294,6 +294,17 @@ def test_gemv_and_gemm_validation():
     assert sk(ctypes.byref(down), FAKE + 8, FAKE, FAKE, need, None) == 3
     assert sk(ctypes.byref(_nv(K=16)), FAKE, FAKE, FAKE, need, None) == 2
     assert sk(ctypes.byref(_nv(layout=1)), FAKE, FAKE, FAKE, need, None) == 5
+    lrs = lib.attnq_gemv_nvfp4_lowrank_splitk                                      # (W0, s, U, V, r, x, t, split_ws, bytes, y)
+    assert lrs(ctypes.byref(down), FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, need, FAKE, None) == 1       # split_ws needed
+    assert lrs(ctypes.byref(down), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, need - 1, FAKE, None) == 2   # too small
+    assert lrs(ctypes.byref(down), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE + 128, need, FAKE, None) == 3  # 256-byte
+    assert lrs(ctypes.byref(down), FAKE, FAKE, FAKE, 65, FAKE, FAKE, FAKE, need, FAKE, None) == 2      # r > 64
+    assert lrs(ctypes.byref(down), FAKE, None, FAKE, 4, FAKE, FAKE, FAKE, need, FAKE, None) == 1       # U missing
+    assert lrs(ctypes.byref(down), FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, need, FAKE, None) == 1       # t missing
+    assert lrs(ctypes.byref(down), FAKE, FAKE, FAKE, 4, FAKE + 8, FAKE, FAKE, need, FAKE, None) == 3   # x 16-byte
+    assert lrs(ctypes.byref(down), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, need, FAKE + 2, None) == 3   # y 4-byte
+    assert lrs(ctypes.byref(_nv(K=16)), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, need, FAKE, None) == 2
+    assert lrs(ctypes.byref(nv), FAKE + 1, FAKE, FAKE, 4, FAKE, FAKE, None, 0, FAKE, None) == 3       # unsplit: s 2-byte
     na = lib.attnq_gemv_nvfp4_splitk_noalloc
     assert na(ctypes.byref(_nv(N=20176, K=16384)), FAKE, FAKE, None) == 2       # 1261 tiles > 1 MiB of records
     assert na(ctypes.byref(_nv(N=20160, K=49152 + 32)), FAKE, FAKE + 2, None) == 3   # unsplit shape: checks still run

@@ -270,3 +270,46 @@ def test_31b_like_shapes_on_sampled_rows(A, N, K, r):
     rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N),
                                      np.random.default_rng(75).choice(N, 400, replace=False)]))
     _check(y, parts, s, U, V, x, K, rows, what)
+
+
+def _run_splitk(A, W, s, U, V, x, split_ws):
+    """attnq_gemv_nvfp4_lowrank_splitk with a fresh NaN-filled t workspace and the given records."""
+    r = 0 if U is None else U.shape[1]
+    y = torch.full((W.N,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = None
+    if r:
+        ws = torch.full((A.attnq_gemv_nvfp4_lowrank_workspace(W.K, len(W.seg_end), r),), float("nan"),
+                        dtype=torch.float32, device="cuda")
+    A.attnq_gemv_nvfp4_lowrank_splitk(W, dev(s), dev(U), dev(V), dev(x.reshape(-1)), ws, split_ws, y)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+# the split-K form (attnq_gemv_nvfp4_lowrank_splitk): 6 slices (K = 21504 and 24576, rank 16 and 64),
+# 5 slices with a ragged last one (K = 16416), rank 0 with s, a two-segment block whose boundary falls
+# inside a row tile, and an unsplit row length (K = 8192, the plain low-rank call), every element
+# against the oracle's bound; a second call on the same records gives the same bits
+@pytest.mark.parametrize("segs,K,r", [((300,), 21504, 16), ((129,), 24576, 64), ((77,), 16416, 3),
+                                      ((300,), 21504, 0), ((150, 301), 21504, 16), ((64,), 8192, 8)])
+def test_lowrank_splitk_vs_oracle(A, segs, K, r):
+    seg_end = list(np.cumsum(segs))
+    N = seg_end[-1]
+    what = f"lowrank split-K {segs}x{K} rank {r}"
+    say(what)
+    W, parts = _shared(A, N, K, 77, seg_end=seg_end)
+    if len(segs) > 1:
+        s, U, V = _segment_factors(seg_end, K, r, 77)
+    else:
+        s, U, V = _factors(N, K, r, 77, 1)
+    x = inputs.activation_bf16(1, K, 9, 77, r)
+    split_ws = A.splitk_workspace(N, K)
+    y = _run_splitk(A, W, s, U, V, x, split_ws)
+    _check(y, parts, s, U, V, x, K, np.arange(N), what)
+    y2 = _run_splitk(A, W, s, U, V, x, split_ws)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), what
+    if r == 0:
+        # with no row terms the epilogue is the split-K GEMV's y times s
+        yp = torch.empty((N,), dtype=torch.float32, device="cuda")
+        A.attnq_gemv_nvfp4_splitk(W, dev(x.reshape(-1)), yp, split_ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(y, (host(yp) * O.bf16_to_f32(s)).astype(np.float32)), what
