@@ -59,7 +59,7 @@ LOWRANK_RANK = 16
 # HBM traffic of one fused gate|up launch from the FETCH_SIZE / WRITE_SIZE passes recorded in
 # profiles/gemv_nvfp4_31b_token_traffic.md (FETCH scaled x1.9999, WRITE x1.0 by a 1 GiB copy).
 # Valid only for the kernel code it was measured on: reported as null once that changes.
-GATE_UP_TRAFFIC = {"sources_sha256_16": "b65c1e9396728b0a", "bytes": 130363209}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "42c01147214a0f99", "bytes": 130371401}
 
 
 def gemv_sources_hash() -> str:
