@@ -21,7 +21,7 @@ projections left in bf16 (attnq_gemv_bf16) and the MLP in NVFP4; and the runtime
 s, U, V in the GEMV epilogue (attnq_gemv_nvfp4_lowrank_splitk; the down projection on the split-K GEMV). Consecutive layers of one band read the
 same block, so part of that stream's block bytes may come from the last-level cache.
 
-Output: one JSON line (see the design doc for the fields). Options:
+Output: one JSON line (metric, value, trials, roofline, per-projection and stream figures). Options:
   --steps K --warmup W       timed / untimed steps (defaults 20 / 5)
   --gpus N                   only N = 1 is supported (one GPU)
   --no-cpu-baseline          skip the oracle timing
